@@ -1,0 +1,13 @@
+"""Float64 CPU oracle for exact softmax attention (test infrastructure only:
+imported by the tests, the smoke check and the benchmark's CPU-baseline leg,
+never by the product path)."""
+from .attention_oracle import (  # noqa: F401
+    backward_dkdv_cols,
+    backward_dq_rows,
+    causal_blocked,
+    dense_backward,
+    dense_forward,
+    forward_rows,
+    online_softmax_step,
+    tiled_forward,
+)

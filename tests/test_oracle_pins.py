@@ -1,0 +1,414 @@
+"""Pins of the float64 oracle against facts fixed outside it.
+
+Each pin is checked against the oracle as it stands, and the mutation tests at
+the bottom plant plausible mistakes in a copy of the oracle's source and check
+that at least one pin catches each of them.
+"""
+import json
+import os
+import types
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import attention_oracle as ao
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "tiled_online_softmax_examples.json")
+
+
+def _f(x):
+    return np.array(x, dtype=object).astype(str).astype(np.float64) if isinstance(x, list) else float(x)
+
+
+@pytest.fixture(scope="module")
+def golden():
+    with open(GOLDEN) as fh:
+        return json.load(fh)
+
+
+def _rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+# --- pin checks, written as functions of an oracle module so that the mutation
+# --- tests can run them against planted mistakes -----------------------------
+
+def pin_example1(mod, g):
+    ex = g["example1_noncausal"]
+    tol = g["printed_digits_tolerance"]["abs"]
+    Q, K, V = _f(ex["Q"]), _f(ex["K"]), _f(ex["V"])
+    o, lse = mod.dense_forward(Q, K, V, 1 / np.sqrt(Q.shape[-1]), causal=False)
+    ok = np.allclose(o, _f(ex["output"]), rtol=0, atol=tol) and np.allclose(lse, _f(ex["lse"]), rtol=0, atol=tol)
+    for b in ex["block_sizes"]:
+        ot, lt = mod.tiled_forward(Q, K, V, b, causal=False)
+        ok = ok and np.allclose(ot, _f(ex["output"]), rtol=0, atol=tol) and np.allclose(lt, _f(ex["lse"]), rtol=0, atol=tol)
+    return ok
+
+
+def pin_example2(mod, g):
+    ex = g["example2_causal"]
+    tol = g["printed_digits_tolerance"]["abs"]
+    Q, K, V = _f(ex["Q"]), _f(ex["K"]), _f(ex["V"])
+    o, lse = mod.dense_forward(Q, K, V, 1 / np.sqrt(Q.shape[-1]), causal=True)
+    ok = np.allclose(o, _f(ex["output"]), rtol=0, atol=tol) and np.allclose(lse, _f(ex["lse"]), rtol=0, atol=tol)
+    ot, lt = mod.tiled_forward(Q, K, V, ex["block_sizes"][0], causal=True)
+    return ok and np.allclose(ot, _f(ex["output"]), rtol=0, atol=tol) and np.allclose(lt, _f(ex["lse"]), rtol=0, atol=tol)
+
+
+def pin_example3(mod, g):
+    ex = g["example3_step"]
+    tol = g["printed_digits_tolerance"]["abs"]
+    m, l, acc = _f(ex["m"]), _f(ex["l"]), _f(ex["acc"])
+    args = (m.copy(), l.copy(), acc.copy(), _f(ex["scores"]), _f(ex["v_block"]))
+    m2, l2, a2 = mod.online_softmax_step(*args)
+    return (np.array_equal(m2, _f(ex["m_new"])) and np.allclose(l2, _f(ex["l_new"]), rtol=0, atol=tol)
+            and np.allclose(a2, _f(ex["acc_new"]), rtol=0, atol=tol))
+
+
+def _loss(mod, q, k, v, do, scale, causal):
+    o, _ = mod.dense_forward(q, k, v, scale, causal)
+    return float(np.sum(do * o))
+
+
+def fd_max_rel_err(mod, seed, tq, tk, d, dv, causal, h=1e-6):
+    """Largest relative error of the oracle backward against central finite
+    differences of L = sum(dO o O) taken through the oracle forward."""
+    r = _rng(seed)
+    q, k, v = r.standard_normal((tq, d)), r.standard_normal((tk, d)), r.standard_normal((tk, dv))
+    do = r.standard_normal((tq, dv))
+    scale = 1 / np.sqrt(d) * 1.3  # a scale other than 1/sqrt(d) exposes a missing factor
+    grads = mod.dense_backward(q, k, v, do, scale, causal)
+    worst = 0.0
+    for x, gx in zip((q, k, v), grads):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            keep = x[idx]
+            x[idx] = keep + h
+            lp = _loss(mod, q, k, v, do, scale, causal)
+            x[idx] = keep - h
+            lm = _loss(mod, q, k, v, do, scale, causal)
+            x[idx] = keep
+            num[idx] = (lp - lm) / (2 * h)
+        denom = max(1.0, float(np.max(np.abs(num))))
+        worst = max(worst, float(np.max(np.abs(num - gx))) / denom)
+    return worst
+
+
+FD_CASES = [(1, 1, 1, 1, 1, False), (2, 3, 4, 2, 3, False), (3, 4, 4, 3, 2, True),
+            (4, 5, 3, 4, 4, True), (5, 3, 5, 2, 2, True), (6, 2, 5, 3, 1, False)]
+
+
+def pin_fd(mod):
+    return all(fd_max_rel_err(mod, *c) < 1e-7 for c in FD_CASES)
+
+
+def torch_reference(q, k, v, do, scale, causal):
+    """torch CPU float64: library SDPA forward, logsumexp, and autograd."""
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(tq[None], tk[None], tv[None], is_causal=causal,
+                                                          scale=scale)[0]
+    s = scale * (tq.detach() @ tk.detach().T)
+    if causal:
+        s = s.masked_fill(torch.ones(s.shape, dtype=torch.bool).triu(1), float("-inf"))
+    lse = torch.logsumexp(s, dim=-1)
+    o.backward(torch.tensor(do))
+    return o.detach().numpy(), lse.numpy(), tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+def pin_torch(mod):
+    ok = True
+    for seed, tq, tk, d, dv, causal in [(11, 17, 23, 8, 5, False), (12, 33, 33, 16, 16, True),
+                                        (13, 9, 40, 4, 7, True), (14, 40, 9, 6, 6, True)]:
+        r = _rng(seed)
+        q, k, v = r.standard_normal((tq, d)), r.standard_normal((tk, d)), r.standard_normal((tk, dv))
+        do = r.standard_normal((tq, dv))
+        scale = 1 / np.sqrt(d)
+        o, lse = mod.dense_forward(q, k, v, scale, causal)
+        dq, dk, dv_ = mod.dense_backward(q, k, v, do, scale, causal)
+        ref = torch_reference(q, k, v, do, scale, causal)
+        for a, b in zip((o, lse, dq, dk, dv_), ref):
+            ok = ok and np.allclose(a, b, rtol=1e-11, atol=1e-11)
+    return ok
+
+
+def pin_block_invariance(mod):
+    ok = True
+    for seed, tq, tk, d, dv in [(21, 64, 64, 64, 64), (22, 5, 37, 3, 9), (23, 37, 5, 8, 2), (24, 1, 1, 1, 1)]:
+        r = _rng(seed)
+        q, k, v = r.standard_normal((tq, d)), r.standard_normal((tk, d)), r.standard_normal((tk, dv))
+        for causal in (False, True):
+            o, lse = mod.dense_forward(q, k, v, 1 / np.sqrt(d), causal)
+            for b in (1, 2, 3, 7, 64, 128):
+                ot, lt = mod.tiled_forward(q, k, v, b, causal)
+                ok = ok and np.max(np.abs(ot - o)) <= 1e-9 and np.max(np.abs(lt - lse)) <= 1e-9
+    return ok
+
+
+def pin_adversarial(mod):
+    """Scores above +1000 in one key block and below -1000 in the next must
+    give finite outputs that agree between the dense and tiled forms."""
+    from exact_tiled_softmax_amd.inputs import adversarial_problem
+    ok = True
+    for high_first in (True, False):
+        q, k, v, _ = (t[0, 0].numpy().astype(np.float64) for t in adversarial_problem(0, 64, 64, 64, 64, 32, high_first))
+        for causal in (False, True):
+            o, lse = mod.dense_forward(q, k, v, 1 / 8.0, causal)
+            ok = ok and bool(np.all(np.isfinite(o)) and np.all(np.isfinite(lse)))
+            for b in (1, 7, 32, 64, 128):
+                ot, lt = mod.tiled_forward(q, k, v, b, causal)
+                ok = ok and np.max(np.abs(ot - o)) <= 1e-9
+                ok = ok and np.max(np.abs(lt - lse)) <= 1e-9 * max(1.0, np.max(np.abs(lse)))
+    return ok
+
+
+# --- the pins, applied to the oracle as it stands -----------------------------
+
+def test_example1_noncausal(golden):
+    assert pin_example1(ao, golden)
+
+
+def test_example2_causal_short_last_block(golden):
+    assert pin_example2(ao, golden)
+
+
+def test_example3_online_step_with_blocked_row(golden):
+    assert pin_example3(ao, golden)
+
+
+def test_step_does_not_modify_inputs(golden):
+    ex = golden["example3_step"]
+    arrs = [_f(ex[k]) for k in ("m", "l", "acc", "scores", "v_block")]
+    before = [a.copy() for a in arrs]
+    ao.online_softmax_step(*arrs)
+    for a, b in zip(arrs, before):
+        assert np.array_equal(a, b)
+
+
+def test_forward_does_not_modify_inputs():
+    r = _rng(5)
+    arrs = [r.standard_normal((6, 4)), r.standard_normal((7, 4)), r.standard_normal((7, 3))]
+    before = [a.copy() for a in arrs]
+    ao.dense_forward(*arrs, 0.5, True)
+    ao.tiled_forward(*arrs, 3, True)
+    ao.dense_backward(*arrs, r.standard_normal((6, 3)), 0.5, True)
+    for a, b in zip(arrs, before):
+        assert np.array_equal(a, b)
+
+
+def test_block_size_invariance():
+    assert pin_block_invariance(ao)
+
+
+@pytest.mark.parametrize("high_first", [True, False])
+@pytest.mark.parametrize("causal", [False, True])
+def test_adversarial_scores_stay_finite_and_exact(high_first, causal):
+    from exact_tiled_softmax_amd.inputs import adversarial_problem
+    q, k, v, _ = (t[0, 0].numpy().astype(np.float64) for t in adversarial_problem(0, 64, 64, 64, 64, 32, high_first))
+    s = (q @ k.T) / 8.0
+    hi = slice(0, 32) if high_first else slice(32, 64)
+    lo = slice(32, 64) if high_first else slice(0, 32)
+    assert s[:, hi].min() > 1000 and s[:, lo].max() < -1000
+    o, lse = ao.dense_forward(q, k, v, 1 / 8.0, causal)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    for b in (1, 7, 32, 64, 128):
+        ot, lt = ao.tiled_forward(q, k, v, b, causal)
+        assert np.max(np.abs(ot - o)) <= 1e-9
+        assert np.max(np.abs(lt - lse)) <= 1e-9 * max(1.0, np.max(np.abs(lse)))
+
+
+@pytest.mark.parametrize("case", FD_CASES)
+def test_backward_matches_finite_differences(case):
+    assert fd_max_rel_err(ao, *case) < 1e-7
+
+
+def test_matches_torch_sdpa_and_autograd_float64():
+    assert pin_torch(ao)
+
+
+# closed forms and special cases
+
+def test_single_key():
+    r = _rng(31)
+    q, k, v = r.standard_normal((5, 3)), r.standard_normal((1, 3)), r.standard_normal((1, 4))
+    o, lse = ao.dense_forward(q, k, v, 0.7, False)
+    assert np.allclose(o, np.repeat(v, 5, axis=0), rtol=0, atol=1e-15)
+    assert np.allclose(lse, 0.7 * (q @ k[0]), rtol=0, atol=1e-14)
+
+
+def test_causal_first_row_sees_only_first_key():
+    r = _rng(32)
+    q, k, v = r.standard_normal((6, 3)), r.standard_normal((6, 3)), r.standard_normal((6, 2))
+    o, lse = ao.dense_forward(q, k, v, 0.5, True)
+    assert np.allclose(o[0], v[0], rtol=0, atol=1e-15)
+    assert np.isclose(lse[0], 0.5 * q[0] @ k[0], rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_queries_average_allowed_values(causal):
+    r = _rng(33)
+    tq, tk = 7, 5
+    q, k, v = np.zeros((tq, 4)), r.standard_normal((tk, 4)), r.standard_normal((tk, 3))
+    o, lse = ao.dense_forward(q, k, v, 0.5, causal)
+    for i in range(tq):
+        n = min(i + 1, tk) if causal else tk
+        assert np.allclose(o[i], v[:n].mean(axis=0), rtol=0, atol=1e-14)
+        assert np.isclose(lse[i], np.log(n), rtol=0, atol=1e-14)
+
+
+def test_equal_value_rows_give_that_row_and_zero_qk_grads():
+    r = _rng(34)
+    q, k = r.standard_normal((6, 4)), r.standard_normal((8, 4))
+    v = np.tile(r.standard_normal((1, 3)), (8, 1))
+    do = r.standard_normal((6, 3))
+    for causal in (False, True):
+        o, _ = ao.dense_forward(q, k, v, 0.5, causal)
+        assert np.allclose(o, v[:6], rtol=0, atol=1e-14)
+        dq, dk, _ = ao.dense_backward(q, k, v, do, 0.5, causal)
+        assert np.max(np.abs(dq)) < 1e-13 and np.max(np.abs(dk)) < 1e-13
+
+
+def test_key_shift_invariance_and_gradient_sums():
+    r = _rng(35)
+    q, k, v = r.standard_normal((9, 5)), r.standard_normal((9, 5)), r.standard_normal((9, 4))
+    do = r.standard_normal((9, 4))
+    u = r.standard_normal(5)
+    for causal in (False, True):
+        o, lse = ao.dense_forward(q, k, v, 0.4, causal)
+        o2, lse2 = ao.dense_forward(q, k + u, v, 0.4, causal)
+        assert np.allclose(o2, o, rtol=0, atol=1e-13)
+        assert np.allclose(lse2 - lse, 0.4 * (q @ u), rtol=0, atol=1e-13)
+        dq, dk, dv = ao.dense_backward(q, k, v, do, 0.4, causal)
+        assert np.allclose(dk.sum(axis=0), 0, atol=1e-13)
+        assert np.allclose(dv.sum(axis=0), do.sum(axis=0), atol=1e-13)
+
+
+def test_key_permutation_noncausal():
+    r = _rng(36)
+    q, k, v = r.standard_normal((5, 4)), r.standard_normal((11, 4)), r.standard_normal((11, 3))
+    do = r.standard_normal((5, 3))
+    perm = r.permutation(11)
+    o, lse = ao.dense_forward(q, k, v, 0.5, False)
+    o2, lse2 = ao.dense_forward(q, k[perm], v[perm], 0.5, False)
+    assert np.allclose(o, o2, atol=1e-14) and np.allclose(lse, lse2, atol=1e-14)
+    _, dk, dv = ao.dense_backward(q, k, v, do, 0.5, False)
+    _, dk2, dv2 = ao.dense_backward(q, k[perm], v[perm], do, 0.5, False)
+    assert np.allclose(dk[perm], dk2, atol=1e-14) and np.allclose(dv[perm], dv2, atol=1e-14)
+
+
+def test_lse_matches_library_logsumexp_by_loops():
+    from scipy.special import logsumexp
+    r = _rng(37)
+    q, k, v = r.standard_normal((4, 3)), r.standard_normal((6, 3)), r.standard_normal((6, 2))
+    _, lse = ao.dense_forward(q, k, v, 0.9, True)
+    for i in range(4):
+        s = [0.9 * sum(q[i, c] * k[j, c] for c in range(3)) for j in range(i + 1)]
+        assert np.isclose(lse[i], logsumexp(s), rtol=0, atol=1e-14)
+
+
+def pin_blocked_row(mod):
+    """"Tiled attention with an online softmax", section "Task": a row with no
+    allowed key yet comes out of the step as m' = -inf, l' = 0, a' = 0."""
+    m = np.array([-np.inf, -np.inf])
+    l = np.zeros(2)
+    acc = np.zeros((2, 3))
+    s = np.full((2, 4), -np.inf)
+    m2, l2, a2 = mod.online_softmax_step(m, l, acc, s, np.ones((4, 3)))
+    return bool(np.all(np.isneginf(m2)) and np.all(l2 == 0) and np.all(a2 == 0))
+
+
+def test_fully_blocked_rows_stay_empty():
+    assert pin_blocked_row(ao)
+
+
+def test_sampled_helpers_match_dense():
+    r = _rng(38)
+    q, k, v = r.standard_normal((40, 6)), r.standard_normal((40, 6)), r.standard_normal((40, 5))
+    do = r.standard_normal((40, 5))
+    for causal in (False, True):
+        o, lse = ao.dense_forward(q, k, v, 0.4, causal)
+        dq, dk, dv = ao.dense_backward(q, k, v, do, 0.4, causal)
+        rows = np.array([0, 7, 39])
+        o_r, lse_r = ao.forward_rows(q, k, v, rows, 0.4, causal)
+        assert np.allclose(o_r, o[rows], atol=1e-14) and np.allclose(lse_r, lse[rows], atol=1e-14)
+        assert np.allclose(ao.backward_dq_rows(q, k, v, do, rows, 0.4, causal), dq[rows], atol=1e-13)
+        dk_c, dv_c = ao.backward_dkdv_cols(q, k, v, do, rows, 0.4, causal, row_chunk=16)
+        assert np.allclose(dk_c, dk[rows], atol=1e-13) and np.allclose(dv_c, dv[rows], atol=1e-13)
+
+
+def test_row_chunking_is_only_memory_bounding():
+    r = _rng(39)
+    q, k, v = r.standard_normal((50, 4)), r.standard_normal((50, 4)), r.standard_normal((50, 3))
+    do = r.standard_normal((50, 3))
+    a = ao.dense_forward(q, k, v, 0.5, True, row_chunk=7)
+    b = ao.dense_forward(q, k, v, 0.5, True, row_chunk=4096)
+    assert np.allclose(a[0], b[0], atol=1e-15) and np.allclose(a[1], b[1], atol=1e-15)
+    a = ao.dense_backward(q, k, v, do, 0.5, True, row_chunk=7)
+    b = ao.dense_backward(q, k, v, do, 0.5, True, row_chunk=4096)
+    for x, y in zip(a, b):
+        assert np.allclose(x, y, atol=1e-14)
+
+
+# --- mutation tests: plant mistakes in a copy of the oracle ------------------
+
+ORACLE_SRC = os.path.join(os.path.dirname(os.path.dirname(__file__)), "oracle", "attention_oracle.py")
+
+MUTANTS = {
+    "drop_rowsum_term_in_dS": ("ds = dp * p - rowsum * p", "ds = dp * p"),
+    "wrong_sign_rowsum_term": ("ds = dp * p - rowsum * p", "ds = dp * p + rowsum * p"),
+    "dq_missing_scale": ("dq[r0:r1] = scale * (ds @ k)", "dq[r0:r1] = (ds @ k)"),
+    "dk_wrong_key_index": ("dk += scale * (ds.T @ q[r0:r1])", "dk += scale * (ds.T[::-1] @ q[r0:r1])"),
+    "dv_wrong_query_index": ("dv += p.T @ do", "dv += p.T @ do[::-1]"),
+    "dp_transposed_value": ("dp = do @ v.T", "dp = do @ v[::-1].T"),
+    "causal_blocks_wrong_side": ("return cols > rows", "return cols < rows"),
+    "causal_blocks_diagonal": ("return cols > rows", "return cols >= rows"),
+    "lse_base2": ("lse = np.where(l > 0, mu + np.log(np.where(l > 0, l, 1.0)), NEG_INF)",
+                  "lse = np.where(l > 0, mu + np.log2(np.where(l > 0, l, 1.0)), NEG_INF)"),
+    "no_max_subtraction_guard": ("mu = np.where(np.isneginf(m), 0.0, m)", "mu = np.where(np.isneginf(m), 0.0, 0.0 * m)"),
+    "step_rescale_wrong_direction": ("c = np.exp(m - shift)", "c = np.exp(shift - m)"),
+    "step_missing_rescale_of_acc": ("acc_new = c[:, None] * acc + p @ v_block", "acc_new = acc + p @ v_block"),
+    "step_no_neg_inf_guard": ("shift = np.where(np.isneginf(m_new), 0.0, m_new)", "shift = m_new"),
+    "tiled_last_block_dropped": ("stop = min(tk, start + block_size)", "stop = start + block_size\n        if stop > tk:\n            break"),
+    "dense_row_norm_missing": ("p = np.where(l > 0, e / np.where(l > 0, l, 1.0), 0.0)", "p = e"),
+    "transposed_pv": ("o[r0:r1] = p @ v", "o[r0:r1] = (p @ v)[:, ::-1]"),
+}
+
+
+def _mutant(name):
+    old, new = MUTANTS[name]
+    src = open(ORACLE_SRC).read()
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    mod = types.ModuleType("oracle_mutant_" + name)
+    exec(compile(src.replace(old, new), ORACLE_SRC + ":" + name, "exec"), mod.__dict__)
+    return mod
+
+
+def _all_pins_pass(mod, g):
+    checks = [
+        lambda: pin_example1(mod, g),
+        lambda: pin_example2(mod, g),
+        lambda: pin_example3(mod, g),
+        lambda: pin_block_invariance(mod),
+        lambda: pin_adversarial(mod),
+        lambda: pin_blocked_row(mod),
+        lambda: pin_torch(mod),
+        lambda: pin_fd(mod),
+    ]
+    for c in checks:
+        try:
+            with np.errstate(all="ignore"):
+                if not c():
+                    return False
+        except Exception:
+            return False
+    return True
+
+
+def test_unmutated_oracle_passes_every_pin(golden):
+    assert _all_pins_pass(ao, golden)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, golden):
+    assert not _all_pins_pass(_mutant(name), golden), f"no pin catches mutant {name}"
