@@ -1,0 +1,173 @@
+"""Thin ctypes binding of libattn.so (include/attn.h).
+
+Argument marshalling only: tensors are passed as device pointers and the
+current torch stream as the hipStream_t; every step of the computation runs in
+the library's HIP kernels.  There is no fallback: if libattn.so is missing or
+the GPU is absent, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("ATTN_LIB", os.path.join(_PKG, "libattn.so"))
+
+ATTN_OK = 0
+ATTN_ERR_INVALID_ARG = -1
+ATTN_ERR_UNSUPPORTED = -2
+ATTN_ERR_HIP = -3
+
+EXPORTED = ("attn_fwd", "attn_fwd_splits", "attn_bwd", "attn_fwd_f32", "attn_bwd_f32", "attn_strerror",
+            "attn_last_hip_error")
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} failed with {code}: {msg}")
+        self.code = code
+
+
+def load() -> ctypes.CDLL:
+    """Load libattn.so once (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} not found: build it with `python -m exact_tiled_softmax_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    dims = [I, I, I, I, I, I, F, I]  # B H Tq Tk d dv scale causal
+    lib.attn_fwd.argtypes = [P, P, P, P, P, *dims, P]
+    lib.attn_fwd_splits.argtypes = [P, P, P, P, P, *dims, I, P]
+    lib.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, *dims, P]
+    lib.attn_fwd_f32.argtypes = [P, P, P, P, P, *dims, I, P]
+    lib.attn_bwd_f32.argtypes = [P, P, P, P, P, P, P, P, P, *dims, P]
+    for fn in ("attn_fwd", "attn_fwd_splits", "attn_bwd", "attn_fwd_f32", "attn_bwd_f32"):
+        getattr(lib, fn).restype = I
+    lib.attn_strerror.argtypes = [I]
+    lib.attn_strerror.restype = ctypes.c_char_p
+    lib.attn_last_hip_error.argtypes = []
+    lib.attn_last_hip_error.restype = I
+    _lib = lib
+    return lib
+
+
+def strerror(code: int) -> str:
+    return load().attn_strerror(code).decode()
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != ATTN_OK:
+        msg = strerror(rc)
+        if rc == ATTN_ERR_HIP:
+            msg += f" (hipError {load().attn_last_hip_error()})"
+        raise AttnError(fn, rc, msg)
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dims(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, T, dim]")
+    B, H, Tq, d = q.shape
+    if k.shape[:2] != (B, H) or v.shape[:2] != (B, H) or k.shape[3] != d or v.shape[2] != k.shape[2]:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    return B, H, Tq, k.shape[2], d, v.shape[3]
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, device) -> None:
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda" or t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def fwd(q, k, v, scale=None, causal=False, out=None, lse=None, num_splits=None):
+    """bf16 forward: returns (o [B,H,Tq,dv] bf16, lse [B,H,Tq] fp32)."""
+    lib = load()
+    B, H, Tq, Tk, d, dv = _dims(q, k, v)
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, torch.bfloat16, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, Tq, dv), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H, Tq), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.bfloat16, dev)
+    _need(lse, "lse", torch.float32, dev)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Tq, Tk, d, dv, float(scale), int(bool(causal)))
+    if num_splits is None:
+        _check("attn_fwd", lib.attn_fwd(*args, _stream(dev)))
+    else:
+        _check("attn_fwd_splits", lib.attn_fwd_splits(*args, int(num_splits), _stream(dev)))
+    return out, lse
+
+
+def bwd(q, k, v, o, lse, dout, scale=None, causal=False, dq=None, dk=None, dv=None):
+    """bf16 backward: returns (dq, dk, dv) bf16 with the shapes of q, k, v."""
+    lib = load()
+    B, H, Tq, Tk, d, dvd = _dims(q, k, v)
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _need(t, n, torch.bfloat16, dev)
+    _need(lse, "lse", torch.float32, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _need(t, n, torch.bfloat16, dev)
+    rc = lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                      B, H, Tq, Tk, d, dvd, float(scale), int(bool(causal)), _stream(dev))
+    _check("attn_bwd", rc)
+    return dq, dk, dv
+
+
+def fwd_f32(q, k, v, scale=None, causal=False, block_n=0, out=None, lse=None):
+    """fp32 forward with the key-block size `block_n` (0 = default)."""
+    lib = load()
+    B, H, Tq, Tk, d, dv = _dims(q, k, v)
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, torch.float32, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty((B, H, Tq, dv), dtype=torch.float32, device=dev) if out is None else out
+    lse = torch.empty((B, H, Tq), dtype=torch.float32, device=dev) if lse is None else lse
+    rc = lib.attn_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Tq, Tk, d, dv, float(scale),
+                          int(bool(causal)), int(block_n), _stream(dev))
+    _check("attn_fwd_f32", rc)
+    return out, lse
+
+
+def bwd_f32(q, k, v, o, lse, dout, scale=None, causal=False):
+    """fp32 backward: returns (dq, dk, dv)."""
+    lib = load()
+    B, H, Tq, Tk, d, dvd = _dims(q, k, v)
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (dout, "dout")):
+        _need(t, n, torch.float32, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    rc = lib.attn_bwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                          B, H, Tq, Tk, d, dvd, float(scale), int(bool(causal)), _stream(dev))
+    _check("attn_bwd_f32", rc)
+    return dq, dk, dv

@@ -1,0 +1,140 @@
+// C ABI front end of libattn.so (declared in include/attn.h): argument checks,
+// kernel choice, stream-ordered workspace, HIP error mapping.  Argument checks
+// run before any HIP call, so an invalid call neither touches the device nor
+// needs one.
+#include <math.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "attn.h"
+#include "attn_launch.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_fail(hipError_t e) {
+  g_last_hip_error = static_cast<int>(e);
+  return ATTN_ERR_HIP;
+}
+
+bool dims_ok(int B, int H, int Tq, int Tk, int d, int dv) {
+  if (B < 1 || H < 1 || Tq < 1 || Tk < 1 || d < 1 || dv < 1) return false;
+  // element counts of every tensor must fit the 64-bit offsets used inside,
+  // and B*H and the workgroup counts must fit an int
+  const int64_t bh = (int64_t)B * H;
+  if (bh > (int64_t)INT32_MAX / 8) return false;
+  if (bh * Tq > (int64_t)INT32_MAX || bh * Tk > (int64_t)INT32_MAX) return false;
+  return true;
+}
+
+bool scale_ok(float s) { return isfinite(s) && s >= 0.f; }
+
+int check_common(const void* q, const void* k, const void* v, const void* o, const void* lse, int B, int H, int Tq,
+                 int Tk, int d, int dv, float scale) {
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_INVALID_ARG;
+  if (!dims_ok(B, H, Tq, Tk, d, dv)) return ATTN_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
+bool bf16_dims_supported(int d, int dv) { return d == dv && (d == 64 || d == 128); }
+
+int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Tq, int Tk, int d,
+             int dv, float scale, int causal, int num_splits, void* stream) {
+  int rc = check_common(q, k, v, o, lse, B, H, Tq, Tk, d, dv, scale);
+  if (rc != ATTN_OK) return rc;
+  if (num_splits < 0) return ATTN_ERR_INVALID_ARG;
+  if (!bf16_dims_supported(d, dv)) return ATTN_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int BH = B * H;
+  const int splits = attn::fwd_bf16_num_splits(BH, Tq, Tk, causal, num_splits);
+  const size_t ws_bytes = attn::fwd_bf16_workspace_bytes(BH, Tq, d, splits);
+  void* ws = nullptr;
+  if (ws_bytes) {
+    hipError_t e = hipMallocAsync(&ws, ws_bytes, s);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  hipError_t e = attn::fwd_bf16_launch(q, k, v, o, lse, BH, Tq, Tk, d, scale, causal, splits, ws, s);
+  if (ws) {
+    hipError_t f = hipFreeAsync(ws, s);
+    if (e == hipSuccess) e = f;
+  }
+  return e == hipSuccess ? ATTN_OK : hip_fail(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Tq, int Tk, int d,
+             int dv, float scale, int causal, void* stream) {
+  return fwd_impl(q, k, v, o, lse, B, H, Tq, Tk, d, dv, scale, causal, 0, stream);
+}
+
+int attn_fwd_splits(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Tq, int Tk,
+                    int d, int dv, float scale, int causal, int num_splits, void* stream) {
+  return fwd_impl(q, k, v, o, lse, B, H, Tq, Tk, d, dv, scale, causal, num_splits, stream);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+             void* dq, void* dk, void* dv_grad, int B, int H, int Tq, int Tk, int d, int dv, float scale, int causal,
+             void* stream) {
+  int rc = check_common(q, k, v, o, lse, B, H, Tq, Tk, d, dv, scale);
+  if (rc != ATTN_OK) return rc;
+  if (!dout || !dq || !dk || !dv_grad) return ATTN_ERR_INVALID_ARG;
+  if (!bf16_dims_supported(d, dv)) return ATTN_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int BH = B * H;
+  void* ws = nullptr;
+  hipError_t e = hipMallocAsync(&ws, attn::bwd_bf16_workspace_bytes(BH, Tq, d), s);
+  if (e != hipSuccess) return hip_fail(e);
+  e = attn::bwd_bf16_launch(q, k, v, o, lse, dout, dq, dk, dv_grad, BH, Tq, Tk, d, scale, causal, ws, s);
+  hipError_t f = hipFreeAsync(ws, s);
+  if (e == hipSuccess) e = f;
+  return e == hipSuccess ? ATTN_OK : hip_fail(e);
+}
+
+int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int Tq, int Tk,
+                 int d, int dv, float scale, int causal, int block_n, void* stream) {
+  int rc = check_common(q, k, v, o, lse, B, H, Tq, Tk, d, dv, scale);
+  if (rc != ATTN_OK) return rc;
+  if (d > 128 || dv > 128) return ATTN_ERR_UNSUPPORTED;
+  if (block_n < 0 || block_n > 1024) return ATTN_ERR_INVALID_ARG;
+  if (block_n == 0) block_n = 64;
+  hipError_t e = attn::fwd_f32_launch(q, k, v, o, lse, B * H, Tq, Tk, d, dv, scale, causal, block_n,
+                                      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : hip_fail(e);
+}
+
+int attn_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* lse, const float* dout,
+                 float* dq, float* dk, float* dv_grad, int B, int H, int Tq, int Tk, int d, int dv, float scale,
+                 int causal, void* stream) {
+  int rc = check_common(q, k, v, o, lse, B, H, Tq, Tk, d, dv, scale);
+  if (rc != ATTN_OK) return rc;
+  if (!dout || !dq || !dk || !dv_grad) return ATTN_ERR_INVALID_ARG;
+  if (d > 128 || dv > 128) return ATTN_ERR_UNSUPPORTED;
+  hipError_t e = attn::bwd_f32_launch(q, k, v, o, lse, dout, dq, dk, dv_grad, B * H, Tq, Tk, d, dv, scale, causal,
+                                      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : hip_fail(e);
+}
+
+const char* attn_strerror(int code) {
+  switch (code) {
+    case ATTN_OK:
+      return "success";
+    case ATTN_ERR_INVALID_ARG:
+      return "invalid argument (null pointer, dimension < 1, non-finite or negative scale, or bad block size)";
+    case ATTN_ERR_UNSUPPORTED:
+      return "unsupported head dimensions for this entry point";
+    case ATTN_ERR_HIP:
+      return "a HIP launch or allocation failed (see attn_last_hip_error)";
+    default:
+      return "unknown error code";
+  }
+}
+
+int attn_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

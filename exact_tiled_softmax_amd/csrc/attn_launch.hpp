@@ -1,0 +1,33 @@
+// Host-side launchers of the attention kernels (internal; the public ABI is
+// include/attn.h).  Each launcher only enqueues kernels on `stream` and returns
+// the launch status; argument checking is done by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace attn {
+
+// ---- bf16 forward ---------------------------------------------------------------
+// Number of key splits to use (requested <= 0: heuristic), clamped to the number
+// of 64-key blocks.
+int fwd_bf16_num_splits(int BH, int Tq, int Tk, int causal, int requested);
+size_t fwd_bf16_workspace_bytes(int BH, int Tq, int d, int num_splits);
+hipError_t fwd_bf16_launch(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Tq,
+                           int Tk, int d, float scale, int causal, int num_splits, void* workspace,
+                           hipStream_t stream);
+
+// ---- bf16 backward --------------------------------------------------------------
+size_t bwd_bf16_workspace_bytes(int BH, int Tq, int d);
+hipError_t bwd_bf16_launch(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                           const void* dout, void* dq, void* dk, void* dv, int BH, int Tq, int Tk, int d,
+                           float scale, int causal, void* workspace, hipStream_t stream);
+
+// ---- fp32 path (block-size faithful forward, deterministic backward) -------------
+hipError_t fwd_f32_launch(const float* q, const float* k, const float* v, float* o, float* lse, int BH, int Tq,
+                          int Tk, int d, int dv, float scale, int causal, int block_n, hipStream_t stream);
+hipError_t bwd_f32_launch(const float* q, const float* k, const float* v, const float* o, const float* lse,
+                          const float* dout, float* dq, float* dk, float* dv_grad, int BH, int Tq, int Tk, int d,
+                          int dv, float scale, int causal, hipStream_t stream);
+
+}  // namespace attn

@@ -126,23 +126,37 @@ def random_problem(seed: int, B: int, H: int, Tq: int, Tk: int, d: int, dv: int,
 
 
 def adversarial_problem(seed: int, Tq: int, Tk: int, d: int, dv: int, split: int, high_first: bool,
-                        alpha: float = 100.0):
-    """fp32 single-head problem whose scores jump between blocks: keys
-    [0, split) get +100 in column 0 and keys [split, 2*split) get -100 (the
-    sign pattern repeats every 2*split keys; reversed when high_first is
-    False).  Column 0 of Q is |q0| + 1 and Q is multiplied by alpha, so with
-    scale 1/sqrt(d) the scores sit well above +1000 in one block and well below
-    -1000 in the next, with about +-100 of noise around them."""
+                        alpha: float = 100.0, separated: bool = True):
+    """fp32 single-head problem whose scores jump between key blocks.
+
+    Column 0 of K is +100 on keys [0, split) and -100 on keys [split, 2*split)
+    (the pattern repeats every 2*split keys; swapped when high_first is
+    False), and column 0 of Q is alpha*(|q0| + 1), so with scale 1/sqrt(d) the
+    scores sit above +1000 in one block and below -1000 in the next.
+
+    separated=True: only column 0 of Q is scaled, and the first key of every
+    block gets +10 more in column 0, so each block has one key whose score
+    leads the others by at least 125 and the softmax of every row is decided
+    by a single key (an fp32 score near 1250 carries about 6e-5 of rounding,
+    which a mix of near-tied keys would pass on to the output).
+    separated=False: all of Q is multiplied by alpha, leaving about +-100 of
+    noise between the keys of a block (near ties occur)."""
     g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([2000 + seed, Tq, Tk, d, dv, split])))
     q = g.standard_normal((Tq, d), dtype=np.float32)
     k = g.standard_normal((Tk, d), dtype=np.float32)
     v = g.standard_normal((Tk, dv), dtype=np.float32)
     do = g.standard_normal((Tq, dv), dtype=np.float32)
     q[:, 0] = np.abs(q[:, 0]) + 1.0
-    q *= np.float32(alpha)
-    hi = (np.arange(Tk) // split) % 2 == 0
+    if separated:
+        q[:, 0] *= np.float32(alpha)
+    else:
+        q *= np.float32(alpha)
+    idx = np.arange(Tk)
+    hi = (idx // split) % 2 == 0
     if not high_first:
         hi = ~hi
     k[:, 0] = np.where(hi, 100.0, -100.0).astype(np.float32)
+    if separated:
+        k[idx % split == 0, 0] += np.float32(10.0)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).reshape((1, 1) + a.shape)
     return t(q), t(k), t(v), t(do)

@@ -1,0 +1,152 @@
+/*
+ * attn.h - C ABI of the exact tiled-softmax attention library (libattn.so)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Every entry point computes exact softmax attention (no approximation):
+ *
+ *   S = scale * Q K^T,  P = row-softmax(S with blocked keys removed),
+ *   O = P V,            LSE_i = log(sum_j exp(S_ij))   (natural log)
+ *
+ * as defined in "The Hidden Recurrence in Softmax Attention: A Path to Flash
+ * Attention", section "Standard Attention / Forward Pass", and "attention
+ * backprop", section "Forward Pass" (the 1/sqrt(head_dim) scale is the caller's
+ * `scale` argument here).  The forward kernels never build S: they visit K/V
+ * block by block and keep, per query row, a running max m, a running sum l and
+ * an accumulator a that are rescaled whenever the max grows ("The Hidden
+ * Recurrence in Softmax Attention", section "Chunk-wise Mode with Online
+ * Softmax Re-scale"; "Tiled attention with an online softmax", section
+ * "Task").  The backward kernels recompute P from the stored LSE instead of
+ * storing it ("The Hidden Recurrence in Softmax Attention", section "Flash
+ * Attention Backward Pass", closing comment) and apply the gradients of
+ * "attention backprop", sections "Gradient of V and P", "Gradient of S" and
+ * "Gradient of Q and K".
+ *
+ * Conventions shared by all entry points
+ * --------------------------------------
+ * Layout.   Tensors are contiguous, row-major [B, H, T, dim] ("attention
+ *           backprop", section "Forward Pass": batch, heads, sequence, head
+ *           dim): q [B,H,Tq,d], k [B,H,Tk,d], v [B,H,Tk,dv], o/dout
+ *           [B,H,Tq,dv], lse [B,H,Tq] (fp32 in every variant).
+ * Pointers. Device pointers (memory of the GPU that is current on the calling
+ *           thread).  The caller owns every buffer.  Inputs are const and never
+ *           written ("Tiled attention with an online softmax", section
+ *           "Constraints": inputs are not changed).  Outputs are overwritten in
+ *           full, never accumulated into.  Outputs must not alias inputs.
+ * Mask.     causal != 0 blocks key j for query i when j > i, on global row
+ *           indices ("Tiled attention with an online softmax", section
+ *           "Task"); with Tq != Tk this is top-left alignment.  causal == 0
+ *           blocks nothing.  A blocked key contributes exactly zero, like a
+ *           score of -infinity.
+ * Scale.    `scale` multiplies Q K^T; callers normally pass 1/sqrt(d).  It
+ *           must be finite and >= 0.
+ * Empty rows. A query row with no allowed key gets O = 0 and LSE = -inf
+ *           (the page's step leaves such a row at m = -inf, l = 0, a = 0).
+ *           With causal top-left masking and Tk >= 1 this never happens.
+ * Stream.   `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *           enqueue work on it and never synchronise; kernel faults surface at
+ *           the caller's next synchronisation on that stream.
+ * Workspace. attn_bwd and (for long key ranges) attn_fwd need scratch memory
+ *           (fp32 dQ accumulator, row sums D, split partial states).  The
+ *           library takes it with hipMallocAsync on `stream` and returns it
+ *           with hipFreeAsync on the same stream, so its lifetime is
+ *           stream-ordered and no state persists between calls.
+ * Errors.   Return 0 on success or a negative ATTN_ERR_* code.  Argument
+ *           checks happen before any HIP call, so an invalid call has no
+ *           effect.  No C++ exception crosses this interface.
+ * Threads.  Calls on different streams may run concurrently.
+ */
+#ifndef EXACT_TILED_SOFTMAX_ATTN_H
+#define EXACT_TILED_SOFTMAX_ATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_OK 0
+#define ATTN_ERR_INVALID_ARG (-1) /* null pointer, dimension < 1, bad scale, bad block size */
+#define ATTN_ERR_UNSUPPORTED (-2) /* head dims the bf16 kernels are not built for */
+#define ATTN_ERR_HIP (-3)         /* a HIP launch or allocation failed */
+
+/*
+ * attn_fwd - bf16 forward.
+ *   q, k, v : bf16 inputs (layout above).
+ *   o       : bf16 output [B,H,Tq,dv], O = P V rounded to nearest even.
+ *   lse     : fp32 output [B,H,Tq], natural-log log-sum-exp of the scaled,
+ *             masked scores ("Tiled attention with an online softmax",
+ *             section "Task": log-sum-exp = m + log l).
+ * Arithmetic: bf16 MFMA products with fp32 accumulation; the online softmax
+ * statistics are fp32; P is rounded to bf16 before the P V product.
+ * Supported: d == dv, d in {64, 128}; otherwise ATTN_ERR_UNSUPPORTED.
+ * B, H, Tq, Tk >= 1 (any value; ragged tails are masked).
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int Tq, int Tk, int d, int dv, float scale, int causal,
+             void* stream);
+
+/*
+ * attn_fwd_splits - attn_fwd with an explicit number of key-range splits.
+ *   num_splits: 0 lets the library choose (what attn_fwd does); n >= 1 splits
+ *   each row's key range into n contiguous chunks processed by separate
+ *   workgroups whose partial states (m, l, a) are merged afterwards with the
+ *   same rescale rule ("The Hidden Recurrence in Softmax Attention", section
+ *   "Chunk-wise Mode with Online Softmax Re-scale").  Values above the number
+ *   of 64-key blocks are clamped.  Other arguments as attn_fwd.
+ */
+int attn_fwd_splits(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int Tq, int Tk, int d, int dv, float scale, int causal,
+                    int num_splits, void* stream);
+
+/*
+ * attn_bwd - bf16 backward.
+ *   q, k, v, o, lse : the forward's inputs and outputs (o bf16, lse fp32).
+ *   dout            : bf16 gradient of the loss with respect to O.
+ *   dq, dk, dv_grad : bf16 outputs with the shapes of q, k, v.
+ * Computes, per (b, h), with P recomputed as exp(S - LSE):
+ *   D_i = sum_c dout_ic o_ic            ("attention backprop", "Gradient of S")
+ *   dV  = P^T dout                      ("attention backprop", "Gradient of V and P")
+ *   dS  = P o (dout V^T - D)            ("attention backprop", "Gradient of S")
+ *   dQ  = scale dS K,  dK = scale dS^T Q ("attention backprop", "Gradient of Q and K",
+ *                                         with the chain-rule factor of `scale`)
+ * dQ is summed over key blocks in an fp32 workspace (device atomics), so its
+ * low bits may vary between runs; dK and dV are deterministic.
+ * Supported: d == dv, d in {64, 128}; otherwise ATTN_ERR_UNSUPPORTED.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv_grad,
+             int B, int H, int Tq, int Tk, int d, int dv, float scale, int causal,
+             void* stream);
+
+/*
+ * attn_fwd_f32 - fp32 forward that follows the page's block loop literally:
+ * keys are taken in blocks of `block_n` starting at 0, block_n, 2*block_n, ...
+ * (the last may be shorter) and each block updates (m, l, a) with one online
+ * softmax step ("Tiled attention with an online softmax", section "Task").
+ *   block_n: 1..1024, or 0 for the default of 64.  Any block size gives the
+ *   same result up to fp32 rounding (section "Constraints").
+ * All tensors fp32.  1 <= d, dv <= 128.
+ */
+int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                 int B, int H, int Tq, int Tk, int d, int dv, float scale, int causal,
+                 int block_n, void* stream);
+
+/*
+ * attn_bwd_f32 - fp32 backward (same formulas as attn_bwd, fp32 throughout,
+ * deterministic, no workspace).  All tensors fp32.  1 <= d, dv <= 128.
+ */
+int attn_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* lse,
+                 const float* dout, float* dq, float* dk, float* dv_grad,
+                 int B, int H, int Tq, int Tk, int d, int dv, float scale, int causal,
+                 void* stream);
+
+/* attn_strerror - static description of a return code (never NULL). */
+const char* attn_strerror(int code);
+
+/* attn_last_hip_error - the hipError_t value behind the most recent
+ * ATTN_ERR_HIP returned on the calling thread (0 if none). */
+int attn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_TILED_SOFTMAX_ATTN_H */

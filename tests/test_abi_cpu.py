@@ -1,0 +1,100 @@
+"""The C-ABI library loads, exports every symbol include/attn.h declares, and
+rejects invalid arguments before any HIP call (so these run without a GPU)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from exact_tiled_softmax_amd import attn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "attn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(attn_\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(attn.LIB_PATH):
+        from exact_tiled_softmax_amd import build
+        build.build()
+    return attn.load()
+
+
+def test_header_declares_the_expected_entry_points():
+    assert set(declared_functions()) == set(attn.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_strerror_covers_codes(lib):
+    for code in (0, -1, -2, -3, 12345):
+        s = attn.strerror(code)
+        assert isinstance(s, str) and s
+    assert lib.attn_last_hip_error() == 0
+
+
+NZ = 16  # a non-null dummy pointer; validation fails before it could be used
+
+
+def fwd_call(lib, q=NZ, k=NZ, v=NZ, o=NZ, lse=NZ, B=1, H=1, Tq=8, Tk=8, d=64, dv=64, scale=0.125, causal=0):
+    return lib.attn_fwd(q, k, v, o, lse, B, H, Tq, Tk, d, dv, scale, causal, None)
+
+
+@pytest.mark.parametrize("kw", [dict(q=None), dict(k=None), dict(v=None), dict(o=None), dict(lse=None),
+                                dict(B=0), dict(H=-1), dict(Tq=0), dict(Tk=0), dict(d=0), dict(dv=0),
+                                dict(scale=float("nan")), dict(scale=float("inf")), dict(scale=-1.0),
+                                dict(B=1 << 20, H=1 << 20)])
+def test_fwd_invalid_args(lib, kw):
+    assert fwd_call(lib, **kw) == attn.ATTN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("d,dv", [(32, 32), (64, 128), (128, 64), (96, 96), (256, 256)])
+def test_fwd_unsupported_head_dims(lib, d, dv):
+    assert fwd_call(lib, d=d, dv=dv) == attn.ATTN_ERR_UNSUPPORTED
+
+
+def test_fwd_splits_rejects_negative(lib):
+    assert lib.attn_fwd_splits(NZ, NZ, NZ, NZ, NZ, 1, 1, 8, 8, 64, 64, 0.1, 0, -1, None) == attn.ATTN_ERR_INVALID_ARG
+
+
+def test_bwd_invalid_and_unsupported(lib):
+    args = [NZ] * 9 + [1, 1, 8, 8, 64, 64, 0.125, 1, None]
+    for i in range(9):
+        a = list(args)
+        a[i] = None
+        assert lib.attn_bwd(*a) == attn.ATTN_ERR_INVALID_ARG
+    a = list(args)
+    a[13] = a[14] = 80
+    assert lib.attn_bwd(*a) == attn.ATTN_ERR_UNSUPPORTED
+    a = list(args)
+    a[15] = math.nan
+    assert lib.attn_bwd(*a) == attn.ATTN_ERR_INVALID_ARG
+
+
+def test_f32_entry_points_validate(lib):
+    base = [NZ] * 5 + [1, 1, 8, 8, 64, 64, 0.125, 0]
+    assert lib.attn_fwd_f32(*base, -1, None) == attn.ATTN_ERR_INVALID_ARG
+    assert lib.attn_fwd_f32(*base, 1025, None) == attn.ATTN_ERR_INVALID_ARG
+    b = list(base)
+    b[9] = 129
+    assert lib.attn_fwd_f32(*b, 0, None) == attn.ATTN_ERR_UNSUPPORTED
+    bb = [NZ] * 9 + [1, 1, 8, 8, 64, 200, 0.125, 0, None]
+    assert lib.attn_bwd_f32(*bb) == attn.ATTN_ERR_UNSUPPORTED
+    bb[5] = None
+    assert lib.attn_bwd_f32(*bb) == attn.ATTN_ERR_INVALID_ARG
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(attn, "_lib", None)
+    monkeypatch.setattr(attn, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        attn.load()

@@ -1,0 +1,198 @@
+"""GPU parity of the HIP kernels (through the C ABI) against the float64 oracle
+on seeded inputs, at sizes the oracle finishes in seconds that still span
+several tiles and ragged tails.
+
+Tolerances (element passes if |x-r| <= tol or |x-r| <= tol*|r|):
+  fp32 entry points: 1e-5 on O, LSE, dQ, dK, dV
+  bf16 entry points: 2e-2 on O, dQ, dK, dV and 1e-2 on LSE
+"""
+import hashlib
+
+import numpy as np
+import pytest
+import torch
+
+from exact_tiled_softmax_amd import attn
+from exact_tiled_softmax_amd.inputs import WORKLOADS, adversarial_problem, exact_f64, make_tensor, random_problem
+from oracle import dense_backward, dense_forward
+from tests._util import assert_close
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-5
+TOL_BF16 = 2e-2
+TOL_LSE_BF16 = 1e-2
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    attn.load()
+    return torch.device("cuda:0")
+
+
+def f64(t):
+    return exact_f64(t)
+
+
+def run_f32(dev, q, k, v, causal, block_n, scale=None):
+    o, lse = attn.fwd_f32(q.to(dev), k.to(dev), v.to(dev), scale=scale, causal=causal, block_n=block_n)
+    torch.cuda.synchronize()
+    return f64(o), f64(lse)
+
+
+# ---- fp32 path: the tiny single-head workload, every block size ---------------
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("block_n", [1, 7, 64, 128])
+def test_f32_tiny_head_all_block_sizes(dev, causal, block_n):
+    w = WORKLOADS["tiny_f32_t64_d64"]
+    q, k, v = (make_tensor(w, n) for n in ("q", "k", "v"))
+    o, lse = run_f32(dev, q, k, v, causal, block_n)
+    ro, rl = dense_forward(f64(q), f64(k), f64(v), w.scale, causal)
+    assert_close("O", o, ro, TOL_F32)
+    assert_close("LSE", lse, rl, TOL_F32)
+
+
+@pytest.mark.parametrize("high_first", [True, False])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("tk,split", [(64, 32), (256, 128)])
+@pytest.mark.parametrize("block_n", [1, 7, 64, 128])
+def test_f32_adversarial_thousand_scores(dev, high_first, causal, tk, split, block_n):
+    q, k, v, _ = adversarial_problem(0, 64, tk, 64, 64, split, high_first)
+    s = f64(q)[0, 0] @ f64(k)[0, 0].T / 8.0
+    assert s.max() > 1000 and s.min() < -1000
+    o, lse = run_f32(dev, q, k, v, causal, block_n)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    ro, rl = dense_forward(f64(q), f64(k), f64(v), 1 / 8.0, causal)
+    assert_close("O", o, ro, TOL_F32)
+    assert_close("LSE", lse, rl, TOL_F32)
+
+
+# Near-tied keys at |s| ~ 1250-5000: an fp32 score there is only known to
+# about ulp(4096)/2 = 2.4e-4 after its own rounding, plus the rounding of a
+# 64-term dot product whose partial sums reach ~4e4 (ulp 3.9e-3, /8 for the
+# scale -> ~5e-4).  Mixing two near-tied keys turns a score error e into an
+# output error of at most e*|v_a - v_b|/4 <~ 1e-3 for |v| < 4; the check
+# allows 5e-3 and still requires every output to be finite.
+TOL_F32_NEAR_TIES = 5e-3
+
+
+@pytest.mark.parametrize("high_first", [True, False])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("block_n", [1, 7, 64, 128])
+def test_f32_adversarial_near_ties(dev, high_first, causal, block_n):
+    q, k, v, _ = adversarial_problem(1, 64, 256, 64, 64, 128, high_first, separated=False)
+    o, lse = run_f32(dev, q, k, v, causal, block_n)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    ro, rl = dense_forward(f64(q), f64(k), f64(v), 1 / 8.0, causal)
+    assert_close("O", o, ro, TOL_F32_NEAR_TIES)
+    assert_close("LSE", lse, rl, TOL_F32)
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 100, 77, 40, 24), (2, 1, 33, 129, 128, 128), (1, 1, 1, 1, 1, 1),
+                                   (1, 3, 50, 20, 16, 100)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_f32_odd_shapes_fwd_bwd(dev, shape, causal):
+    B, H, Tq, Tk, d, dv = shape
+    q, k, v, do = random_problem(7, B, H, Tq, Tk, d, dv, "f32")
+    o, lse = attn.fwd_f32(q.to(dev), k.to(dev), v.to(dev), causal=causal, block_n=13)
+    dq, dk, dvv = attn.bwd_f32(q.to(dev), k.to(dev), v.to(dev), o, lse, do.to(dev), causal=causal)
+    torch.cuda.synchronize()
+    sc = 1 / np.sqrt(d)
+    ro, rl = dense_forward(f64(q), f64(k), f64(v), sc, causal)
+    rq, rk, rv = dense_backward(f64(q), f64(k), f64(v), f64(do), sc, causal)
+    assert_close("O", f64(o), ro, TOL_F32)
+    assert_close("LSE", f64(lse), rl, TOL_F32)
+    assert_close("dQ", f64(dq), rq, TOL_F32)
+    assert_close("dK", f64(dk), rk, TOL_F32)
+    assert_close("dV", f64(dvv), rv, TOL_F32)
+
+
+def test_f32_tiny_head_backward(dev):
+    w = WORKLOADS["tiny_f32_t64_d64"]
+    q, k, v, do = (make_tensor(w, n) for n in ("q", "k", "v", "do"))
+    for causal in (False, True):
+        o, lse = attn.fwd_f32(q.to(dev), k.to(dev), v.to(dev), causal=causal)
+        g = attn.bwd_f32(q.to(dev), k.to(dev), v.to(dev), o, lse, do.to(dev), causal=causal)
+        torch.cuda.synchronize()
+        ref = dense_backward(f64(q), f64(k), f64(v), f64(do), w.scale, causal)
+        for name, x, r in zip(("dQ", "dK", "dV"), g, ref):
+            assert_close(name, f64(x), r, TOL_F32)
+
+
+# ---- bf16 path ---------------------------------------------------------------
+
+BF16_SHAPES = [
+    (1, 2, 300, 333, 64, 64),     # several 256-row query tiles / 64-key tiles, ragged
+    (2, 1, 513, 257, 128, 128),   # Tq > Tk
+    (1, 2, 200, 700, 128, 128),   # Tq < Tk
+    (1, 1, 1, 1, 128, 128),       # single query, single key
+    (1, 1, 1, 300, 64, 64),       # single query row
+    (1, 1, 300, 1, 64, 64),       # single key
+    (1, 1, 64, 64, 128, 128),     # exactly one tile
+]
+
+
+def bf16_problem(shape, seed=3, sigma_q=1.0):
+    B, H, Tq, Tk, d, dv = shape
+    return random_problem(seed, B, H, Tq, Tk, d, dv, "bf16", sigma_q=sigma_q)
+
+
+@pytest.mark.parametrize("shape", BF16_SHAPES)
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_fwd_small(dev, shape, causal):
+    q, k, v, _ = bf16_problem(shape)
+    o, lse = attn.fwd(q.to(dev), k.to(dev), v.to(dev), causal=causal)
+    torch.cuda.synchronize()
+    ro, rl = dense_forward(f64(q), f64(k), f64(v), 1 / np.sqrt(shape[4]), causal)
+    assert_close("O", f64(o), ro, TOL_BF16)
+    assert_close("LSE", f64(lse), rl, TOL_LSE_BF16)
+
+
+@pytest.mark.parametrize("splits", [2, 3, 7, 100])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_fwd_key_splits(dev, splits, causal):
+    shape = (1, 2, 130, 1000, 128, 128)
+    q, k, v, _ = bf16_problem(shape, seed=5, sigma_q=2.0)
+    o, lse = attn.fwd(q.to(dev), k.to(dev), v.to(dev), causal=causal, num_splits=splits)
+    torch.cuda.synchronize()
+    ro, rl = dense_forward(f64(q), f64(k), f64(v), 1 / np.sqrt(128), causal)
+    assert_close("O", f64(o), ro, TOL_BF16)
+    assert_close("LSE", f64(lse), rl, TOL_LSE_BF16)
+
+
+@pytest.mark.parametrize("shape", BF16_SHAPES)
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_bwd_small(dev, shape, causal):
+    q, k, v, do = bf16_problem(shape, seed=4)
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    o, lse = attn.fwd(qd, kd, vd, causal=causal)
+    dq, dk, dv = attn.bwd(qd, kd, vd, o, lse, dod, causal=causal)
+    torch.cuda.synchronize()
+    rq, rk, rv = dense_backward(f64(q), f64(k), f64(v), f64(do), 1 / np.sqrt(shape[4]), causal)
+    assert_close("dQ", f64(dq), rq, TOL_BF16)
+    assert_close("dK", f64(dk), rk, TOL_BF16)
+    assert_close("dV", f64(dv), rv, TOL_BF16)
+
+
+def test_bf16_inputs_unchanged_and_forward_deterministic(dev):
+    q, k, v, do = bf16_problem((1, 2, 300, 333, 128, 128), seed=9)
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    digest = lambda ts: [hashlib.sha256(t.view(torch.int16).cpu().numpy().tobytes()).hexdigest() for t in ts]
+    before = digest((qd, kd, vd, dod))
+    o1, l1 = attn.fwd(qd, kd, vd, causal=True)
+    o2, l2 = attn.fwd(qd, kd, vd, causal=True)
+    attn.bwd(qd, kd, vd, o1, l1, dod, causal=True)
+    torch.cuda.synchronize()
+    assert digest((qd, kd, vd, dod)) == before
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_bf16_scale_zero_gives_mean_of_allowed_values(dev):
+    q, k, v, _ = bf16_problem((1, 1, 70, 70, 64, 64), seed=10)
+    o, lse = attn.fwd(q.to(dev), k.to(dev), v.to(dev), scale=0.0, causal=True)
+    torch.cuda.synchronize()
+    ro, rl = dense_forward(f64(q), f64(k), f64(v), 0.0, True)
+    assert_close("O", f64(o), ro, TOL_BF16)
+    assert_close("LSE", f64(lse), rl, TOL_LSE_BF16)
