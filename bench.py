@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Benchmark of exact tiled-softmax attention on one MI355X.
+
+Metric: attention TFLOP/s for the forward and for forward+backward, bf16,
+d = 128, L = 8192, causal, and the fraction of the dense bf16 MFMA peak.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+attn_fwd (O, LSE) followed by attn_bwd (dQ, dK, dV), on the workload
+B=2, H=32, Tq=Tk=8192, d=dv=128, causal, Q/K/V/dO ~ N(0,1) in bf16, scale
+1/sqrt(d).  Inputs are resident in HBM before the timed region starts.
+
+Throughput counts algorithmic flops only: with `pairs` the number of unmasked
+(query, key) pairs, forward = 2*pairs*(d+dv) (Q K^T and P V) and backward =
+2*pairs*(3d+2dv) (Q K^T recomputed, dO V^T, P^T dO, dS K, dS^T Q).
+
+Prints one JSON line.  Also reports the dominant kernel against its roofline
+(HIP-event durations recorded by the library on the launch stream) and the
+float64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+HEADLINE = "causal_bf16_b2h32_t8192_d128"
+METRIC = "attention TFLOP/s fwd & fwd+bwd, bf16 d=128 L=8192 causal; % of MFMA peak"
+
+
+def unmasked_pairs(tq: int, tk: int, causal: bool) -> int:
+    """(query, key) pairs that are not blocked, per head (causal: key <= query)."""
+    if not causal:
+        return tq * tk
+    n = min(tq, tk)
+    # rows 0..n-1 see i+1 keys; rows n..tq-1 see all tk keys
+    return n * (n + 1) // 2 + (tq - n) * tk
+
+
+def work(w):
+    pairs = unmasked_pairs(w.Tq, w.Tk, w.causal) * w.B * w.H
+    fwd = 2 * pairs * (w.d + w.dv)
+    bwd = 2 * pairs * (3 * w.d + 2 * w.dv)
+    e = 2  # bf16 bytes
+    bh = w.B * w.H
+    fwd_bytes = bh * (e * (w.Tq * w.d + w.Tk * w.d + w.Tk * w.dv + w.Tq * w.dv) + 4 * w.Tq)
+    bwd_bytes = bh * (e * (2 * w.Tq * w.d + 2 * w.Tk * w.d + 2 * w.Tk * w.dv + 2 * w.Tq * w.dv) + 4 * w.Tq)
+    return pairs, fwd, bwd, fwd_bytes, bwd_bytes
+
+
+def kernel_source_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "exact_tiled_softmax_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {"fwd": ["fwd_bf16.hip", "attn_common.hpp"], "bwd": ["bwd_bf16.hip", "attn_common.hpp"]}
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it was
+    taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{kernel}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_src = re.search(r"kernel_source_digest:\s*([0-9a-f]+)", txt)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_src or not m_b or m_src.group(1) != kernel_source_digest(KERNEL_SOURCES[kernel]):
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(w, budget_s: float):
+    """The float64 oracle (dense forward + backward) on whole heads of the
+    workload, as many heads as fit in about `budget_s` seconds (at least one)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from exact_tiled_softmax_amd.inputs import make_head
+    from oracle import dense_backward, dense_forward
+
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done = []
+    flops = 0
+    elapsed = 0.0
+    per_head_pairs = unmasked_pairs(w.Tq, w.Tk, w.causal)
+    for b, h in heads:
+        q, k, v, do = (make_head(w, n, b, h) for n in ("q", "k", "v", "do"))
+        t0 = time.perf_counter()
+        o, lse = dense_forward(q, k, v, w.scale, w.causal)
+        dq, dk, dv = dense_backward(q, k, v, do, w.scale, w.causal)
+        elapsed += time.perf_counter() - t0
+        assert np.isfinite(o).all() and np.isfinite(dq).all()
+        done.append((b, h))
+        flops += 2 * per_head_pairs * ((w.d + w.dv) + (3 * w.d + 2 * w.dv))
+        if elapsed >= budget_s:
+            break
+    threads = 1
+    for info in threadpool_info():
+        if info.get("user_api") == "blas":
+            threads = max(threads, int(info.get("num_threads", 1)))
+    return {
+        "value": flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{len(done)} of {w.B * w.H} heads of {w.name} (first: b,h={done[0]}), forward+backward in "
+                   f"float64 numpy with full score rows, {elapsed:.1f} s; same algorithmic flop count as the GPU"),
+    }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle work (0 = skip)")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); the "
+              "attention kernels have no multi-GPU path in this build", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from exact_tiled_softmax_amd import attn
+    from exact_tiled_softmax_amd.inputs import WORKLOADS, make_tensor
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    attn.load()
+    w = WORKLOADS[args.workload]
+    if w.dtype != "bf16":
+        print("bench.py times the bf16 path", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    print(f"[bench] building inputs for {w.name}", file=sys.stderr, flush=True)
+    q, k, v, do = (make_tensor(w, n).to(dev) for n in ("q", "k", "v", "do"))
+    o = torch.empty((w.B, w.H, w.Tq, w.dv), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.H, w.Tq), dtype=torch.float32, device=dev)
+    dq, dk, dvg = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+    def step():
+        attn.fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse)
+        attn.bwd(q, k, v, o, lse, do, scale=w.scale, causal=w.causal, dq=dq, dk=dk, dv=dvg)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    attn.profile_start()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    attn.profile_stop()
+    kern = {name: attn.profile_query(kind) for kind, name in attn.KERNEL_NAMES.items()}
+
+    pairs, fwd_fl, bwd_fl, fwd_b, bwd_b = work(w)
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    total_tflops = (fwd_fl + bwd_fl) / (ms_step * 1e-3) / 1e12
+    fwd_ms = (kern["fwd"][0] + kern["fwd_combine"][0]) / args.steps
+    bwd_ms = (kern["bwd_preprocess"][0] + kern["bwd"][0] + kern["bwd_finalize"][0]) / args.steps
+    fwd_tflops = fwd_fl / (fwd_ms * 1e-3) / 1e12 if fwd_ms > 0 else None
+    bwd_tflops = bwd_fl / (bwd_ms * 1e-3) / 1e12 if bwd_ms > 0 else None
+
+    # dominant kernel: largest recorded time
+    dom = max(("fwd", "bwd"), key=lambda n: kern[n][0])
+    dom_avg_ms = kern[dom][0] / max(1, kern[dom][1])
+    dom_flops = fwd_fl if dom == "fwd" else bwd_fl
+    achieved = dom_flops / (dom_avg_ms * 1e-3) / 1e12
+    traffic = measured_traffic(dom, w.name)
+    roofline = {
+        "kernel": f"{dom}_bf16_kernel",
+        "bound": "mfma",
+        "achieved": round(achieved, 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "traffic": traffic,
+        "avg_launch_ms": round(dom_avg_ms, 4),
+        "launches": kern[dom][1],
+        "algorithmic_flops_per_launch": dom_flops,
+        "algorithmic_bytes_per_launch": fwd_b if dom == "fwd" else bwd_b,
+    }
+
+    cpu = None
+    if args.cpu_budget > 0:
+        print(f"[bench] timing the CPU oracle (~{args.cpu_budget:.0f} s)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, args.cpu_budget)
+
+    line = {
+        "metric": METRIC,
+        "value": round(total_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Tq": w.Tq, "Tk": w.Tk, "d": w.d, "dv": w.dv,
+                   "causal": w.causal, "step": "attn_fwd + attn_bwd"},
+        "fwd_tflops": round(fwd_tflops, 2) if fwd_tflops else None,
+        "fwd_frac_of_peak": round(fwd_tflops / PEAK_BF16_TFLOPS, 4) if fwd_tflops else None,
+        "bwd_tflops": round(bwd_tflops, 2) if bwd_tflops else None,
+        "bwd_frac_of_peak": round(bwd_tflops / PEAK_BF16_TFLOPS, 4) if bwd_tflops else None,
+        "fwd_bwd_frac_of_peak": round(total_tflops / PEAK_BF16_TFLOPS, 4),
+        "kernel_ms_per_step": {n: round(kern[n][0] / args.steps, 4) for n in kern},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -22,7 +22,15 @@ ATTN_ERR_UNSUPPORTED = -2
 ATTN_ERR_HIP = -3
 
 EXPORTED = ("attn_fwd", "attn_fwd_splits", "attn_bwd", "attn_fwd_f32", "attn_bwd_f32", "attn_strerror",
-            "attn_last_hip_error")
+            "attn_last_hip_error", "attn_profile_start", "attn_profile_stop", "attn_profile_query")
+
+# kernel kinds of attn_profile_query (include/attn.h)
+KERNEL_FWD = 0
+KERNEL_FWD_COMBINE = 1
+KERNEL_BWD_PREPROCESS = 2
+KERNEL_BWD = 3
+KERNEL_BWD_FINALIZE = 4
+KERNEL_NAMES = {0: "fwd", 1: "fwd_combine", 2: "bwd_preprocess", 3: "bwd", 4: "bwd_finalize"}
 
 _lib = None
 
@@ -54,6 +62,12 @@ def load() -> ctypes.CDLL:
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_last_hip_error.argtypes = []
     lib.attn_last_hip_error.restype = I
+    lib.attn_profile_start.argtypes = []
+    lib.attn_profile_start.restype = I
+    lib.attn_profile_stop.argtypes = []
+    lib.attn_profile_stop.restype = I
+    lib.attn_profile_query.argtypes = [I, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
+    lib.attn_profile_query.restype = I
     _lib = lib
     return lib
 
@@ -171,3 +185,20 @@ def bwd_f32(q, k, v, o, lse, dout, scale=None, causal=False):
                           B, H, Tq, Tk, d, dvd, float(scale), int(bool(causal)), _stream(dev))
     _check("attn_bwd_f32", rc)
     return dq, dk, dv
+
+
+def profile_start() -> None:
+    """Start recording HIP events around every kernel the library launches."""
+    _check("attn_profile_start", load().attn_profile_start())
+
+
+def profile_stop() -> None:
+    _check("attn_profile_stop", load().attn_profile_stop())
+
+
+def profile_query(kind: int):
+    """(total_ms, launches) of the kernels of `kind` recorded since profile_start()."""
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_int(0)
+    _check("attn_profile_query", load().attn_profile_query(int(kind), ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value

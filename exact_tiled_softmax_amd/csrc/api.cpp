@@ -5,6 +5,10 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+#include <vector>
+
 #include <hip/hip_runtime.h>
 
 #include "attn.h"
@@ -64,9 +68,109 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
 }
 
+// ---- event profiler ----------------------------------------------------------
+struct Prof {
+  std::mutex mu;
+  std::atomic<bool> on{false};
+  std::vector<hipEvent_t> pool;                       // free events
+  std::vector<hipEvent_t> open[ATTN_KERNEL_KINDS];     // begin event of the launch in flight (per kind)
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> done[ATTN_KERNEL_KINDS];
+  double total_ms[ATTN_KERNEL_KINDS] = {};
+  int launches[ATTN_KERNEL_KINDS] = {};
+};
+Prof& prof() {
+  static Prof* p = new Prof();  // never destroyed: events may outlive static teardown
+  return *p;
+}
+
+hipEvent_t prof_event(Prof& p) {
+  if (!p.pool.empty()) {
+    hipEvent_t e = p.pool.back();
+    p.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
 }  // namespace
 
+namespace attn {
+
+void prof_begin(int kind, hipStream_t stream) {
+  Prof& p = prof();
+  if (!p.on.load(std::memory_order_relaxed)) return;
+  std::lock_guard<std::mutex> g(p.mu);
+  hipEvent_t e = prof_event(p);
+  if (!e) return;
+  if (hipEventRecord(e, stream) != hipSuccess) {
+    p.pool.push_back(e);
+    return;
+  }
+  p.open[kind].push_back(e);
+}
+
+void prof_end(int kind, hipStream_t stream) {
+  Prof& p = prof();
+  if (!p.on.load(std::memory_order_relaxed)) return;
+  std::lock_guard<std::mutex> g(p.mu);
+  if (p.open[kind].empty()) return;
+  hipEvent_t b = p.open[kind].back();
+  p.open[kind].pop_back();
+  hipEvent_t e = prof_event(p);
+  if (!e || hipEventRecord(e, stream) != hipSuccess) {
+    p.pool.push_back(b);
+    if (e) p.pool.push_back(e);
+    return;
+  }
+  p.done[kind].emplace_back(b, e);
+}
+
+}  // namespace attn
+
 extern "C" {
+
+int attn_profile_start(void) {
+  Prof& p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  for (int k = 0; k < ATTN_KERNEL_KINDS; ++k) {
+    for (auto& be : p.done[k]) {
+      p.pool.push_back(be.first);
+      p.pool.push_back(be.second);
+    }
+    p.done[k].clear();
+    p.total_ms[k] = 0.0;
+    p.launches[k] = 0;
+  }
+  p.on.store(true);
+  return ATTN_OK;
+}
+
+int attn_profile_stop(void) {
+  prof().on.store(false);
+  return ATTN_OK;
+}
+
+int attn_profile_query(int kind, double* total_ms, int* launches) {
+  if (kind < 0 || kind >= ATTN_KERNEL_KINDS || !total_ms || !launches) return ATTN_ERR_INVALID_ARG;
+  Prof& p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  for (auto& be : p.done[kind]) {
+    hipError_t e = hipEventSynchronize(be.second);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, be.first, be.second);
+    if (e != hipSuccess) return hip_fail(e);
+    p.total_ms[kind] += ms;
+    p.launches[kind] += 1;
+    p.pool.push_back(be.first);
+    p.pool.push_back(be.second);
+  }
+  p.done[kind].clear();
+  *total_ms = p.total_ms[kind];
+  *launches = p.launches[kind];
+  return ATTN_OK;
+}
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Tq, int Tk, int d,
              int dv, float scale, int causal, void* stream) {

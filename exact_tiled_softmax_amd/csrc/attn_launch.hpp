@@ -8,6 +8,11 @@
 
 namespace attn {
 
+// Event profiler hooks (defined in api.cpp).  When profiling is off these are
+// a single relaxed load each.
+void prof_begin(int kind, hipStream_t stream);
+void prof_end(int kind, hipStream_t stream);
+
 // ---- bf16 forward ---------------------------------------------------------------
 // Number of key splits to use (requested <= 0: heuristic), clamped to the number
 // of 64-key blocks.

@@ -339,20 +339,26 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(const float* __restri
 template <int D>
 hipError_t bwd_launch_d(const BwdArgs& args, const __bf16* o, __bf16* dq, bool causal, hipStream_t stream) {
   const int rows = args.BH * args.Tq;
+  prof_begin(2, stream);
   hipLaunchKernelGGL(bwd_preprocess_kernel<D>, dim3((rows * 16 + 255) / 256), dim3(256), 0, stream, o, args.dout,
                      const_cast<float*>(args.dsum), args.dq_acc, rows);
+  prof_end(2, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n = args.BH * args.num_kblocks;
+  prof_begin(3, stream);
   if (causal)
     hipLaunchKernelGGL((bwd_bf16_kernel<D, true>), dim3(n), dim3(kBwdThreads), 0, stream, args);
   else
     hipLaunchKernelGGL((bwd_bf16_kernel<D, false>), dim3(n), dim3(kBwdThreads), 0, stream, args);
+  prof_end(3, stream);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t n8 = (size_t)rows * D / 8;
+  prof_begin(4, stream);
   hipLaunchKernelGGL(bwd_finalize_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, args.dq_acc, dq,
                      args.scale, n8);
+  prof_end(4, stream);
   return hipGetLastError();
 }
 

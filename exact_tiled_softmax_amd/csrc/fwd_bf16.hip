@@ -334,7 +334,9 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(const float* __restric
 template <int D, bool CAUSAL, bool SPLIT>
 hipError_t launch_fwd(const FwdArgs& args, hipStream_t stream) {
   const int n = args.BH * args.num_qtiles * args.num_splits;
+  prof_begin(0, stream);
   hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, SPLIT>), dim3(n), dim3(kFwdThreads), 0, stream, args);
+  prof_end(0, stream);
   return hipGetLastError();
 }
 
@@ -394,12 +396,14 @@ hipError_t fwd_bf16_launch(const void* q, const void* k, const void* v, void* o,
   if (e != hipSuccess || !split) return e;
   const int rows = BH * Tq;
   const int blocks = (rows + 3) / 4;
+  prof_begin(1, stream);
   if (d == 128)
     hipLaunchKernelGGL(fwd_combine_kernel<128>, dim3(blocks), dim3(256), 0, stream, args.part_acc, args.part_ml,
                        args.o, lse, BH, Tq, num_splits);
   else
     hipLaunchKernelGGL(fwd_combine_kernel<64>, dim3(blocks), dim3(256), 0, stream, args.part_acc, args.part_ml,
                        args.o, lse, BH, Tq, num_splits);
+  prof_end(1, stream);
   return hipGetLastError();
 }
 

@@ -138,6 +138,29 @@ int attn_bwd_f32(const float* q, const float* k, const float* v, const float* o,
                  int B, int H, int Tq, int Tk, int d, int dv, float scale, int causal,
                  void* stream);
 
+/*
+ * Kernel timing with HIP events (measurement support, not part of the math).
+ * While profiling is on, every kernel the library launches is bracketed by a
+ * pair of hipEvents recorded on the stream it is launched on; the elapsed
+ * times are summed per kernel kind.  Recording adds two event records per
+ * launch and no synchronisation.
+ *   attn_profile_start()  clear the totals and turn recording on
+ *   attn_profile_stop()   turn recording off (recorded pairs are kept)
+ *   attn_profile_query(kind, &total_ms, &launches)
+ *       wait for the recorded events of `kind` (ATTN_KERNEL_*), add their
+ *       durations to the totals and return them.  ATTN_ERR_INVALID_ARG for
+ *       an unknown kind or null pointers, ATTN_ERR_HIP if an event fails.
+ */
+#define ATTN_KERNEL_FWD 0            /* forward main kernel */
+#define ATTN_KERNEL_FWD_COMBINE 1    /* merge of key-split partial states */
+#define ATTN_KERNEL_BWD_PREPROCESS 2 /* D = rowsum(dO o O), dQ workspace clear */
+#define ATTN_KERNEL_BWD 3            /* backward main kernel */
+#define ATTN_KERNEL_BWD_FINALIZE 4   /* dQ workspace -> bf16 */
+#define ATTN_KERNEL_KINDS 5
+int attn_profile_start(void);
+int attn_profile_stop(void);
+int attn_profile_query(int kind, double* total_ms, int* launches);
+
 /* attn_strerror - static description of a return code (never NULL). */
 const char* attn_strerror(int code);
 
