@@ -59,6 +59,28 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 // Value held by lane (l ^ 32).
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
 
+// max / sum of the values held by lanes l and l ^ 32.  v_permlane32_swap(v, v)
+// returns, in its two results, the lower-half and upper-half value of every
+// lane pair (lane order of the pair differs per half, which max and + ignore).
+__device__ __forceinline__ float pair_max(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+// Byte permute: result byte i = byte sel[i] of the 8-byte value {hi:lo}.
+__device__ __forceinline__ unsigned perm_b32(unsigned hi, unsigned lo, unsigned sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+// {lo16(a), lo16(b)} and {hi16(a), hi16(b)} of two packed bf16 pairs.
+__device__ __forceinline__ unsigned pack_lo16(unsigned a, unsigned b) { return perm_b32(b, a, 0x05040100u); }
+__device__ __forceinline__ unsigned pack_hi16(unsigned a, unsigned b) { return perm_b32(b, a, 0x07060302u); }
+
 // Map the hardware workgroup id to a logical work item so that logical items
 // that are adjacent in number run on the same XCD (workgroups are dealt to
 // the 8 XCDs round robin, and each XCD has its own L2).  Logical items

@@ -6,20 +6,34 @@
 // Attention", section "Chunk-wise Mode with Online Softmax Re-scale": query
 // tiles outside, key tiles inside).  Each wave owns 32 rows and keeps, per
 // row, the running max m, running sum l and accumulator a of "Tiled attention
-// with an online softmax", section "Task", entirely in registers.  K/V are
-// streamed in tiles of 64 keys through double-buffered LDS.
+// with an online softmax", section "Task", in registers.  K/V are streamed in
+// tiles of 64 keys through double-buffered LDS; each tile is consumed as two
+// 32-key online-softmax steps.
 //
-// Per K/V tile and wave:
+// Per 32-key step and wave:
 //   S^T = K Q^T           32x32x16 bf16 MFMA, fp32 accumulators, keys on the
 //                         M side so that every lane holds one query row's
-//                         scores in registers (row max/sum need only one
-//                         exchange between the two lane halves)
+//                         scores in registers (a row reduction is 16 registers
+//                         plus one exchange between the lane halves)
 //   mask                  causal (key > query) and ragged tails -> blocked
-//   m' = max(m, rowmax)   log2 domain: scores are multiplied by scale*log2(e)
-//   mu = (m' == -inf) ? 0 : m'      (the page's guard for rows with no key yet)
-//   alpha = exp2(m - mu), P = exp2(s - mu), l = alpha*l + rowsum(P)
-//   a = alpha*a + V^T P^T  P rounded to bf16; V read transposed from LDS
+//   m  = max(m, rowmax)   scores in log2 units (multiplied by scale*log2(e))
+//   P  = exp2(s - m), l += rowsum(P), a += V^T P^T  (P rounded to bf16)
 // Epilogue: O = a / l, LSE = (m + log2 l) * ln 2.
+//
+// The reference max m used in the exponent is only moved when a row's block
+// max exceeds it by more than kTau (log2 units); then l and a are rescaled by
+// exp2(m_old - m_new) as in the page's recurrence.  Between moves P <= 2^kTau,
+// and O = a / l and LSE = m + log2 l are the same quantities for any m (the
+// result is exact; only fp32 rounding differs).  This keeps the 64-register
+// rescale of a off the common path.  A row with no allowed key yet keeps
+// m = -inf and uses 0 in its exponent (the page's guard).
+//
+// LDS layout per stage: K row-major [64][D+8] (MFMA A operand rows, 16-byte
+// reads); V transposed, V^T[c][64 keys] with rows of 80 elements, the 4-key
+// groups of each 16-key MFMA step ordered so that the 8 keys one lane feeds
+// into an MFMA are contiguous, and the 16-byte units XOR-swizzled by (c >> 3)
+// (conflict-free 16-byte reads and at most 2-way conflicts on the 8-byte
+// transposing writes).
 //
 // With key splits, each workgroup covers one contiguous key range and stores
 // its unnormalised state (m, l, a) in fp32; a second kernel merges the states
@@ -35,43 +49,87 @@ constexpr int kFwdWaves = 8;
 constexpr int kFwdThreads = kFwdWaves * 64;
 constexpr int kBM = 32 * kFwdWaves;  // query rows per workgroup
 constexpr int kBN = 64;              // keys per K/V tile
+constexpr int kVtStr = 80;           // V^T row stride (elements)
+constexpr float kTau = 8.f;          // lazy-rescale threshold (log2 units)
 
 template <int D>
 struct FwdCfg {
-  static constexpr int KS = D / 16;                    // MFMA k-steps over the head dim
-  static constexpr int CB = D / 32;                    // 32-wide blocks of the value dim
-  static constexpr int STR = D + 8;                    // LDS row stride (elements)
-  static constexpr int TILE = kBN * STR;               // elements per K or V tile
-  static constexpr int CHUNKS = kBN * D / 8;           // 16-byte chunks per tile
-  static constexpr int PER_THREAD = CHUNKS / kFwdThreads;
-  static_assert(CHUNKS % kFwdThreads == 0, "tile must split evenly over threads");
+  static constexpr int KS = D / 16;                  // MFMA k-steps over the head dim
+  static constexpr int CB = D / 32;                  // 32-wide blocks of the value dim
+  static constexpr int KSTR = D + 8;                 // K row stride (elements)
+  static constexpr int KTILE = kBN * KSTR;           // elements of a K stage
+  static constexpr int VTILE = D * kVtStr;           // elements of a V^T stage
+  static constexpr int STAGE = KTILE + VTILE;
+  static constexpr int KCHUNKS = kBN * D / 8;        // 16-byte chunks of a K tile
+  static constexpr int KPER = KCHUNKS / kFwdThreads;
+  static constexpr int VTASKS = kBN * D / 16;        // 4 keys x 4 columns per task
+  static_assert(KCHUNKS % kFwdThreads == 0, "K tile must split evenly over threads");
+  static_assert(VTASKS <= kFwdThreads, "one V task per thread at most");
 };
 
+// position of 4-key group G (0..15) inside a V^T row: swap bits 0 and 1, so
+// groups (8b+4u+h) and (8b+4u+2+h) become adjacent (one lane's 8 keys)
+__device__ __forceinline__ int vt_group_pos(int g) { return (g & ~3) | ((g & 1) << 1) | ((g >> 1) & 1); }
+
+// element offset of (column c, 16-byte unit U) in a V^T stage
+__device__ __forceinline__ int vt_off(int c, int unit) { return c * kVtStr + ((unit ^ ((c >> 3) & 7)) << 3); }
+
 template <int D>
-__device__ __forceinline__ void load_tile_regs(const __bf16* __restrict__ base, int key0, int key_lim,
-                                               int tid, u32x4 (&r)[FwdCfg<D>::PER_THREAD]) {
-  constexpr int CPR = D / 8;  // chunks per row
+struct TileRegs {
+  u32x4 k[FwdCfg<D>::KPER];
+  u32x2 v[4];
+};
+
+// Global -> registers for one K/V tile (keys >= key_lim read as zero).
+template <int D>
+__device__ __forceinline__ void load_tile(const __bf16* __restrict__ Kh, const __bf16* __restrict__ Vh, int key0,
+                                          int key_lim, int tid, TileRegs<D>& r) {
+  using C = FwdCfg<D>;
+  constexpr int CPR = D / 8;
 #pragma unroll
-  for (int i = 0; i < FwdCfg<D>::PER_THREAD; ++i) {
+  for (int i = 0; i < C::KPER; ++i) {
     const int c = tid + i * kFwdThreads;
     const int row = c / CPR, col = (c % CPR) * 8;
     const int key = key0 + row;
-    if (key < key_lim) {
-      r[i] = *reinterpret_cast<const u32x4*>(base + (size_t)key * D + col);
-    } else {
-      r[i] = u32x4{0u, 0u, 0u, 0u};
+    r.k[i] = key < key_lim ? *reinterpret_cast<const u32x4*>(Kh + (size_t)key * D + col) : u32x4{0u, 0u, 0u, 0u};
+  }
+  if (tid < C::VTASKS) {
+    constexpr int CG = D / 4;  // column groups
+    const int kg = tid / CG, cg = tid % CG;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int key = key0 + 4 * kg + j;
+      r.v[j] = key < key_lim ? *reinterpret_cast<const u32x2*>(Vh + (size_t)key * D + 4 * cg) : u32x2{0u, 0u};
     }
   }
 }
 
+// Registers -> LDS stage: K rows as is, V transposed into V^T.
 template <int D>
-__device__ __forceinline__ void store_tile_lds(__bf16* lds, int tid, const u32x4 (&r)[FwdCfg<D>::PER_THREAD]) {
+__device__ __forceinline__ void store_tile(__bf16* stage, int tid, const TileRegs<D>& r) {
+  using C = FwdCfg<D>;
   constexpr int CPR = D / 8;
 #pragma unroll
-  for (int i = 0; i < FwdCfg<D>::PER_THREAD; ++i) {
+  for (int i = 0; i < C::KPER; ++i) {
     const int c = tid + i * kFwdThreads;
     const int row = c / CPR, col = (c % CPR) * 8;
-    *reinterpret_cast<u32x4*>(lds + row * FwdCfg<D>::STR + col) = r[i];
+    *reinterpret_cast<u32x4*>(stage + row * C::KSTR + col) = r.k[i];
+  }
+  if (tid < C::VTASKS) {
+    constexpr int CG = D / 4;
+    const int kg = tid / CG, cg = tid % CG;
+    const int pos = vt_group_pos(kg);
+    __bf16* vt = stage + C::KTILE;
+    // r.v[j] = {c0 c1 | c2 c3} of key 4kg+j; write {k0 k1 | k2 k3} of each column
+    const u32x2 w0 = {pack_lo16(r.v[0][0], r.v[1][0]), pack_lo16(r.v[2][0], r.v[3][0])};
+    const u32x2 w1 = {pack_hi16(r.v[0][0], r.v[1][0]), pack_hi16(r.v[2][0], r.v[3][0])};
+    const u32x2 w2 = {pack_lo16(r.v[0][1], r.v[1][1]), pack_lo16(r.v[2][1], r.v[3][1])};
+    const u32x2 w3 = {pack_hi16(r.v[0][1], r.v[1][1]), pack_hi16(r.v[2][1], r.v[3][1])};
+    const int c0 = 4 * cg, unit = pos >> 1, half = (pos & 1) * 4;
+    *reinterpret_cast<u32x2*>(vt + vt_off(c0 + 0, unit) + half) = w0;
+    *reinterpret_cast<u32x2*>(vt + vt_off(c0 + 1, unit) + half) = w1;
+    *reinterpret_cast<u32x2*>(vt + vt_off(c0 + 2, unit) + half) = w2;
+    *reinterpret_cast<u32x2*>(vt + vt_off(c0 + 3, unit) + half) = w3;
   }
 }
 
@@ -88,13 +146,121 @@ struct FwdArgs {
   float scale_log2;  // scale * log2(e)
 };
 
+// One 64-key tile for one wave: S^T for both 32-key blocks, row max and
+// reference-max update, then P and a += V^T P^T block by block.
+//
+// Blocked keys (need_mask: causal diagonal or ragged tail) are handled by
+// scaling the scores in place and writing -inf for blocked ones, after which
+// the shared code runs with a unit scale: exp2(-inf - mu) = 0 exactly, also
+// when scale == 0.  A row with no allowed key yet (m_ref = -inf) uses mu = 0.
+template <int D>
+__device__ __forceinline__ void fwd_tile(const __bf16* Ks, const __bf16* Vt, const bf16x8 (&qf)[D / 16],
+                                         f32x16 (&acc)[D / 32], float& m_ref, float& l_run, float c, int lr, int hf,
+                                         bool need_mask, int key_r0, int kend, int row, bool causal) {
+  using C = FwdCfg<D>;
+  f32x16 s0 = f32x16{}, s1 = f32x16{};
+  {
+    bf16x8 kf[C::KS];
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+      kf[ks] = *reinterpret_cast<const bf16x8*>(Ks + lr * C::KSTR + 16 * ks + 8 * hf);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) s0 = mfma32(kf[ks], qf[ks], s0);
+  }
+  {
+    bf16x8 kf[C::KS];
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+      kf[ks] = *reinterpret_cast<const bf16x8*>(Ks + (32 + lr) * C::KSTR + 16 * ks + 8 * hf);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) s1 = mfma32(kf[ks], qf[ks], s1);
+  }
+  bf16x8 vf[2][C::CB];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb) vf[u][cb] = *reinterpret_cast<const bf16x8*>(Vt + vt_off(32 * cb + lr, 2 * u + hf));
+
+  float cc = c;
+  if (need_mask) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = key_r0 + 8 * (r / 4) + (r % 4);
+      s0[r] = (key >= kend || (causal && key > row)) ? -INFINITY : s0[r] * c;
+      s1[r] = (key + 32 >= kend || (causal && key + 32 > row)) ? -INFINITY : s1[r] * c;
+    }
+    cc = 1.f;
+  }
+  // ---- row max and reference-max update -----------------------------------------
+  float mx = fmaxf(s0[0], s1[0]);
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+  mx = pair_max(mx);
+  const float mt = (mx == -INFINITY) ? -INFINITY : mx * cc;
+  const bool move = mt > m_ref + kTau;
+  if (__builtin_amdgcn_ballot_w64(move)) {
+    const float m_new = move ? mt : m_ref;
+    const float alpha = move ? fast_exp2(m_ref - m_new) : 1.f;  // m_ref = -inf -> 0
+    l_run *= alpha;
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[cb][r] *= alpha;
+    m_ref = m_new;
+  }
+  const float mu = (m_ref == -INFINITY) ? 0.f : m_ref;
+  // ---- block 0: P, row sum, a += V^T P^T ------------------------------------------
+  float psum = 0.f;
+  bf16x8 p0, p1;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float x = fast_exp2(__builtin_fmaf(s0[e], cc, -mu));
+    const float y = fast_exp2(__builtin_fmaf(s0[8 + e], cc, -mu));
+    psum += x + y;
+    p0[e] = to_bf16(x);
+    p1[e] = to_bf16(y);
+  }
+#pragma unroll
+  for (int cb = 0; cb < C::CB; ++cb) acc[cb] = mfma32(vf[0][cb], p0, acc[cb]);
+#pragma unroll
+  for (int cb = 0; cb < C::CB; ++cb) acc[cb] = mfma32(vf[1][cb], p1, acc[cb]);
+  // ---- block 1 --------------------------------------------------------------------
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb)
+      vf[u][cb] = *reinterpret_cast<const bf16x8*>(Vt + vt_off(32 * cb + lr, 4 + 2 * u + hf));
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float x = fast_exp2(__builtin_fmaf(s1[e], cc, -mu));
+    const float y = fast_exp2(__builtin_fmaf(s1[8 + e], cc, -mu));
+    psum += x + y;
+    p0[e] = to_bf16(x);
+    p1[e] = to_bf16(y);
+  }
+  l_run += psum;
+#pragma unroll
+  for (int cb = 0; cb < C::CB; ++cb) acc[cb] = mfma32(vf[0][cb], p0, acc[cb]);
+#pragma unroll
+  for (int cb = 0; cb < C::CB; ++cb) acc[cb] = mfma32(vf[1][cb], p1, acc[cb]);
+#if ATTN_FWD_SCHED
+  // interleave the second block's exponentials (VALU) with the first block's
+  // P V MFMAs
+#pragma unroll
+  for (int i = 0; i < 2 * C::CB; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+  }
+#endif
+}
+
 template <int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   using C = FwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 lds[4 * C::TILE];  // K0 V0 K1 V1
+  __shared__ __attribute__((aligned(16))) __bf16 lds[2 * C::STAGE];
 
   const int tid = threadIdx.x;
-  const int wave = tid / 64, lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   const int lr = lane % 32, hf = lane / 32;
   const int n_items = a.BH * a.num_qtiles * a.num_splits;
   const int item = xcd_remap(blockIdx.x, n_items);
@@ -117,8 +283,10 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   }
   if (CAUSAL) kend = min(kend, q0 + kBM);
   const int ntiles = kend > kbeg ? (kend - kbeg + kBN - 1) / kBN : 0;
-  // last key this wave's rows may see (causal), used to skip whole tiles
+  // end of the keys this wave's rows may see (causal): whole tiles past it are
+  // skipped
   const int wave_kend = CAUSAL ? min(kend, q0 + wave * 32 + 32) : kend;
+  const int wave_row0 = q0 + wave * 32;
 
   // Q fragments (B operand of S^T = K Q^T): lane holds Q[row][16*ks + 8*hf + 0..7]
   bf16x8 qf[C::KS];
@@ -135,130 +303,35 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   f32x16 acc[C::CB];
 #pragma unroll
   for (int cb = 0; cb < C::CB; ++cb) acc[cb] = f32x16{};
-  float m_run = -INFINITY;  // running max of scaled scores, log2 units
+  float m_ref = -INFINITY;  // reference max of scaled scores, log2 units
   float l_run = 0.f;        // this lane's share of the running sum
+  const float c = a.scale_log2;
 
-  u32x4 kr[C::PER_THREAD], vr[C::PER_THREAD];
+  TileRegs<D> tr;
   if (ntiles > 0) {
-    load_tile_regs<D>(Kh, kbeg, kend, tid, kr);
-    load_tile_regs<D>(Vh, kbeg, kend, tid, vr);
-    store_tile_lds<D>(lds, tid, kr);
-    store_tile_lds<D>(lds + C::TILE, tid, vr);
+    load_tile<D>(Kh, Vh, kbeg, kend, tid, tr);
+    store_tile<D>(lds, tid, tr);
   }
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
     const int key0 = kbeg + t * kBN;
-    const __bf16* Ks = lds + (t & 1) * 2 * C::TILE;
-    const __bf16* Vs = Ks + C::TILE;
+    const __bf16* Ks = lds + (t & 1) * C::STAGE;
+    const __bf16* Vt = Ks + C::KTILE;
     const bool more = t + 1 < ntiles;
-    if (more) {
-      load_tile_regs<D>(Kh, key0 + kBN, kend, tid, kr);
-      load_tile_regs<D>(Vh, key0 + kBN, kend, tid, vr);
-    }
+    if (more) load_tile<D>(Kh, Vh, key0 + kBN, kend, tid, tr);
 
     if (key0 < wave_kend) {
-      // ---- S^T = K Q^T : two 32-key blocks -----------------------------------
-      f32x16 s[2];
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        s[blk] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (32 * blk + lr) * C::STR + 16 * ks + 8 * hf);
-          s[blk] = mfma32(kf, qf[ks], s[blk]);
-        }
-      }
-      // ---- mask: causal and ragged key tail ----------------------------------
-      const bool need_mask = (key0 + kBN > kend) || (CAUSAL && key0 + kBN - 1 > q0 + wave * 32);
-      if (need_mask) {
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + 32 * blk + 8 * (r / 4) + 4 * hf + (r % 4);
-            const bool blocked = key >= kend || (CAUSAL && key > row);
-            s[blk][r] = blocked ? -INFINITY : s[blk][r];
-          }
-      }
-      // ---- running max -----------------------------------------------------------
-      float mx = -INFINITY;
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[blk][r]);
-      mx = fmaxf(mx, swap_halves(mx));
-      const float mt = (mx == -INFINITY) ? -INFINITY : mx * a.scale_log2;
-      const float m_new = fmaxf(m_run, mt);
-      const float mu = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - mu);
-      m_run = m_new;
-      // ---- P = exp2(s*scale*log2e - mu), row sum -------------------------------
-      float psum = 0.f;
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(__builtin_fmaf(s[blk][r], a.scale_log2, -mu));
-          s[blk][r] = p;
-          psum += p;
-        }
-      if (need_mask) {  // blocked scores must contribute exactly zero (also when scale == 0)
-        psum = 0.f;
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + 32 * blk + 8 * (r / 4) + 4 * hf + (r % 4);
-            const bool blocked = key >= kend || (CAUSAL && key > row);
-            s[blk][r] = blocked ? 0.f : s[blk][r];
-            psum += s[blk][r];
-          }
-      }
-      l_run = l_run * alpha + psum;
-      // rescale the accumulator only when some row of the wave changed its max
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-        for (int cb = 0; cb < C::CB; ++cb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[cb][r] *= alpha;
-      }
-      // ---- P^T as bf16 B operands: k-slot 8*hf+e of (blk,u) <-> key
-      //      32*blk + 16*u + (e<4 ? 4*hf+e : 8+4*hf+e-4)
-      bf16x8 pb[2][2];
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pb[blk][u][e] = to_bf16(s[blk][8 * u + e]);
-      // ---- a += V^T P^T ----------------------------------------------------------
-      const int g16 = lane % 16, csub = (lane / 16) % 2;
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int r0 = 32 * blk + 16 * u + 4 * hf + g16 / 4;
-#pragma unroll
-          for (int cb = 0; cb < C::CB; ++cb) {
-            const int c0 = 32 * cb + 16 * csub + 4 * (g16 % 4);
-            const i16x4 lo = lds_read_tr(Vs + r0 * C::STR + c0);
-            const i16x4 hi = lds_read_tr(Vs + (r0 + 8) * C::STR + c0);
-            acc[cb] = mfma32(join_tr(lo, hi), pb[blk][u], acc[cb]);
-          }
-        }
+      const bool need_mask = (key0 + kBN > kend) || (CAUSAL && key0 + kBN - 1 > wave_row0);
+      fwd_tile<D>(Ks, Vt, qf, acc, m_ref, l_run, c, lr, hf, need_mask, key0 + 4 * hf, kend, row, CAUSAL);
     }
 
-    if (more) {
-      __bf16* Kn = lds + ((t + 1) & 1) * 2 * C::TILE;
-      store_tile_lds<D>(Kn, tid, kr);
-      store_tile_lds<D>(Kn + C::TILE, tid, vr);
-    }
+    if (more) store_tile<D>(lds + ((t + 1) & 1) * C::STAGE, tid, tr);
     __syncthreads();
   }
 
   // ---- epilogue ------------------------------------------------------------------
-  const float l_tot = l_run + swap_halves(l_run);
+  const float l_tot = pair_sum(l_run);
   if (SPLIT) {
     if (row < a.Tq) {
       const size_t prow = ((size_t)split * a.BH + bh) * a.Tq + row;
@@ -267,12 +340,12 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
       for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int c = 32 * cb + 8 * g + 4 * hf;
-          *reinterpret_cast<f32x4*>(pa + c) =
+          const int cc = 32 * cb + 8 * g + 4 * hf;
+          *reinterpret_cast<f32x4*>(pa + cc) =
               f32x4{acc[cb][4 * g], acc[cb][4 * g + 1], acc[cb][4 * g + 2], acc[cb][4 * g + 3]};
         }
       if (hf == 0) {
-        a.part_ml[prow * 2 + 0] = m_run;
+        a.part_ml[prow * 2 + 0] = m_ref;
         a.part_ml[prow * 2 + 1] = l_tot;
       }
     }
@@ -285,13 +358,13 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
     for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int c = 32 * cb + 8 * g + 4 * hf;
+        const int cc = 32 * cb + 8 * g + 4 * hf;
         u32x2 w = {pack_bf16x2(acc[cb][4 * g] * inv, acc[cb][4 * g + 1] * inv),
                    pack_bf16x2(acc[cb][4 * g + 2] * inv, acc[cb][4 * g + 3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + c) = w;
+        *reinterpret_cast<u32x2*>(orow + cc) = w;
       }
     if (hf == 0) {
-      a.lse[(size_t)bh * a.Tq + row] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
+      a.lse[(size_t)bh * a.Tq + row] = l_tot > 0.f ? (m_ref + fast_log2(l_tot)) * kLn2 : -INFINITY;
     }
   }
 }
