@@ -128,6 +128,9 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle work (0 = skip)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB three times (the reference kernel "
+                         "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes) and exit")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -142,6 +145,15 @@ def main(argv=None) -> int:
     from exact_tiled_softmax_amd.inputs import WORKLOADS, make_tensor
 
     assert torch.cuda.is_available(), "bench.py needs the GPU"
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)  # one elementwise kernel: reads n bytes, writes n bytes
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "launches": 3}))
+        return 0
     attn.load()
     w = WORKLOADS[args.workload]
     if w.dtype != "bf16":
