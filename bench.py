@@ -46,6 +46,19 @@ def unmasked_pairs(tq: int, tk: int, causal: bool) -> int:
     return n * (n + 1) // 2 + (tq - n) * tk
 
 
+def kernel_flops(w):
+    """Per kernel: (algorithmic flops it carries, flops it executes).  The
+    backward's algorithmic flops (Q K^T recomputed, dO V^T, P^T dO, dS K,
+    dS^T Q) are split between its two kernels: dK/dV carries Q K^T, dO V^T,
+    P^T dO and dS^T Q; dQ carries dS K and executes Q K^T and dO V^T again."""
+    pairs = unmasked_pairs(w.Tq, w.Tk, w.causal) * w.B * w.H
+    return {
+        "fwd": (2 * pairs * (w.d + w.dv), 2 * pairs * (w.d + w.dv)),
+        "bwd_dkdv": (2 * pairs * (2 * w.d + 2 * w.dv), 2 * pairs * (2 * w.d + 2 * w.dv)),
+        "bwd_dq": (2 * pairs * w.d, 2 * pairs * (2 * w.d + w.dv)),
+    }
+
+
 def work(w):
     pairs = unmasked_pairs(w.Tq, w.Tk, w.causal) * w.B * w.H
     fwd = 2 * pairs * (w.d + w.dv)
@@ -65,13 +78,15 @@ def kernel_source_digest(files):
     return h.hexdigest()[:16]
 
 
-KERNEL_SOURCES = {"fwd": ["fwd_bf16.hip", "attn_common.hpp"], "bwd": ["bwd_bf16.hip", "attn_common.hpp"]}
+KERNEL_SOURCES = {"fwd": ["fwd_bf16.hip", "attn_common.hpp"], "bwd_dkdv": ["bwd_bf16.hip", "attn_common.hpp"],
+                  "bwd_dq": ["bwd_bf16.hip", "attn_common.hpp"]}
+KERNEL_SYMBOL = {"fwd": "fwd_bf16_kernel", "bwd_dkdv": "bwd_dkdv_kernel", "bwd_dq": "bwd_dq_kernel"}
 
 
 def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it was
     taken on the current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{kernel}_{workload}.md")
+    path = os.path.join(ROOT, "profiles", f"{KERNEL_SYMBOL[kernel]}_{workload}.md")
     if not os.path.exists(path):
         return None
     txt = open(path).read()
@@ -189,18 +204,19 @@ def main(argv=None) -> int:
     ms_step = (t1 - t0) * 1e3 / args.steps
     total_tflops = (fwd_fl + bwd_fl) / (ms_step * 1e-3) / 1e12
     fwd_ms = (kern["fwd"][0] + kern["fwd_combine"][0]) / args.steps
-    bwd_ms = (kern["bwd_preprocess"][0] + kern["bwd"][0] + kern["bwd_finalize"][0]) / args.steps
+    bwd_ms = (kern["bwd_prep"][0] + kern["bwd_dkdv"][0] + kern["bwd_dq"][0]) / args.steps
     fwd_tflops = fwd_fl / (fwd_ms * 1e-3) / 1e12 if fwd_ms > 0 else None
     bwd_tflops = bwd_fl / (bwd_ms * 1e-3) / 1e12 if bwd_ms > 0 else None
 
     # dominant kernel: largest recorded time
-    dom = max(("fwd", "bwd"), key=lambda n: kern[n][0])
+    kfl = kernel_flops(w)
+    dom = max(("fwd", "bwd_dkdv", "bwd_dq"), key=lambda n: kern[n][0])
     dom_avg_ms = kern[dom][0] / max(1, kern[dom][1])
-    dom_flops = fwd_fl if dom == "fwd" else bwd_fl
-    achieved = dom_flops / (dom_avg_ms * 1e-3) / 1e12
+    alg_fl, exe_fl = kfl[dom]
+    achieved = alg_fl / (dom_avg_ms * 1e-3) / 1e12
     traffic = measured_traffic(dom, w.name)
     roofline = {
-        "kernel": f"{dom}_bf16_kernel",
+        "kernel": KERNEL_SYMBOL[dom],
         "bound": "mfma",
         "achieved": round(achieved, 2),
         "peak": PEAK_BF16_TFLOPS,
@@ -209,7 +225,9 @@ def main(argv=None) -> int:
         "traffic": traffic,
         "avg_launch_ms": round(dom_avg_ms, 4),
         "launches": kern[dom][1],
-        "algorithmic_flops_per_launch": dom_flops,
+        "algorithmic_flops_per_launch": alg_fl,
+        "executed_flops_per_launch": exe_fl,
+        "executed_tflops": round(exe_fl / (dom_avg_ms * 1e-3) / 1e12, 2),
         "algorithmic_bytes_per_launch": fwd_b if dom == "fwd" else bwd_b,
     }
 

@@ -192,7 +192,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int BH = B * H;
   void* ws = nullptr;
-  hipError_t e = hipMallocAsync(&ws, attn::bwd_bf16_workspace_bytes(BH, Tq, d), s);
+  hipError_t e = hipMallocAsync(&ws, attn::bwd_bf16_workspace_bytes(BH, Tq, Tk, d), s);
   if (e != hipSuccess) return hip_fail(e);
   e = attn::bwd_bf16_launch(q, k, v, o, lse, dout, dq, dk, dv_grad, BH, Tq, Tk, d, scale, causal, ws, s);
   hipError_t f = hipFreeAsync(ws, s);

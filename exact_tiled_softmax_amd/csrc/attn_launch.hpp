@@ -23,7 +23,7 @@ hipError_t fwd_bf16_launch(const void* q, const void* k, const void* v, void* o,
                            hipStream_t stream);
 
 // ---- bf16 backward --------------------------------------------------------------
-size_t bwd_bf16_workspace_bytes(int BH, int Tq, int d);
+size_t bwd_bf16_workspace_bytes(int BH, int Tq, int Tk, int d);
 hipError_t bwd_bf16_launch(const void* q, const void* k, const void* v, const void* o, const float* lse,
                            const void* dout, void* dq, void* dk, void* dv, int BH, int Tq, int Tk, int d,
                            float scale, int causal, void* workspace, hipStream_t stream);

@@ -10,19 +10,29 @@
 // dK = dS^T Q ("Gradient of Q and K"), each of dQ and dK times `scale` because
 // the scores are scale * Q K^T.
 //
-// Kernels:
-//   bwd_preprocess  D_i = sum_c dO_ic O_ic (fp32) and zero the fp32 dQ workspace
-//   bwd_bf16_kernel one workgroup (4 waves) per 128 keys of one (batch, head);
-//                   each wave keeps its 32 keys' K, V rows as MFMA operands and
-//                   its dK^T, dV^T accumulators in registers, and walks the
-//                   query tiles (64 rows) that can see those keys:
-//                     S  = Q K^T, dP = dO V^T   (queries on the M side)
-//                     P  = exp2(S*scale*log2e - LSE*log2e), dS = P o (dP - D)
-//                     dV^T += dO^T P, dK^T += Q^T dS  (Q, dO read transposed
-//                                                      from LDS)
-//                     dS^T -> LDS; dQ_tile += dS K over the 128 keys, added to
-//                     the fp32 workspace with device atomics
-//   bwd_finalize    dQ = scale * workspace, rounded to bf16
+// dK/dV and dQ are reductions over different axes (over queries and over
+// keys), so they come from two kernels that each keep their own accumulator
+// in registers and write it once; no workgroup adds into another's output.
+// Kernels, in launch order:
+//   bwd_stats      per query row: LSE * log2(e) (+inf for a row that is
+//                  outside Tq or has no allowed key, so its P is 0) and
+//                  D = sum_c dO_c O_c, blocked 32 rows at a time
+//   bwd_transpose  Q^T, dO^T, K^T ([d][T], T padded to 64 with zeros) into the
+//                  workspace, with the rows of every 16-row group in the
+//                  order the MFMA operands below take them
+//   bwd_dkdv       one workgroup (4 waves) per 128 keys; each wave keeps its
+//                  32 keys' K and V rows as MFMA operands and dK^T, dV^T in
+//                  registers and walks 32-query tiles streamed into LDS:
+//                    S = Q K^T, dP = dO V^T, P = exp2(S*scale*log2e - LSE2),
+//                    dS = P o (dP - D), dV^T += dO^T P, dK^T += Q^T dS
+//   bwd_dq         one workgroup (8 waves) per 256 queries; each wave keeps
+//                  its 32 queries' Q and dO rows as MFMA operands and dQ^T in
+//                  registers and walks 64-key tiles streamed into LDS:
+//                    S^T = K Q^T, dP^T = V dO^T, dS^T as above,
+//                    dQ^T += K^T dS^T
+// Every LDS operand is read with 16-byte reads from a tile whose 16-byte
+// chunks are XOR-swizzled per row, and tiles are copied global -> LDS by the
+// direct-to-LDS vector load, several tiles ahead of the compute.
 #include "attn_common.hpp"
 #include "attn_launch.hpp"
 
@@ -30,256 +40,314 @@ namespace attn {
 
 namespace {
 
-constexpr int kBwdWaves = 4;
-constexpr int kBwdThreads = kBwdWaves * 64;
-constexpr int kBK = 32 * kBwdWaves;  // keys per workgroup
-constexpr int kBQ = 64;              // query rows per inner tile
+typedef __attribute__((address_space(3))) const void lds_cvoid;
 
-template <int D>
-struct BwdCfg {
-  static constexpr int KS = D / 16;
-  static constexpr int CB = D / 32;
-  static constexpr int STR = D + 8;            // LDS row stride of Q, dO, K tiles
-  static constexpr int STRS = kBQ + 8;         // LDS row stride of the dS^T tile
-  static constexpr int QCHUNKS = kBQ * D / 8;  // 16-byte chunks of a Q or dO tile
-  static constexpr int QPER = QCHUNKS / kBwdThreads;
-  static constexpr int KCHUNKS = kBK * D / 8;
-  static constexpr int KPER = KCHUNKS / kBwdThreads;
-  // dQ output blocks (2 query blocks x CB column blocks) shared by the waves
-  static constexpr int QBLK_PER_WAVE = (2 * CB) / kBwdWaves;
-  static_assert(QCHUNKS % kBwdThreads == 0 && KCHUNKS % kBwdThreads == 0, "tile split");
-  static_assert((2 * CB) % kBwdWaves == 0, "dQ block split");
-};
+// One wave copies 16 bytes per lane from `src` (per lane) to LDS; lane l's
+// bytes land at lds_base + 16*l (lds_base must be the same in every lane).
+// Issued as inline assembly so that the compiler neither reorders LDS
+// accesses across it nor adds waits of its own for it: every copy is waited
+// for explicitly (wait_vm) before a barrier that publishes the tile.
+__device__ __forceinline__ void dma16(const __bf16* src, const __bf16* lds_base) {
+  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_cvoid*)lds_base));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Workgroup barrier that also keeps the compiler from moving memory accesses
+// across it (the tile copies are waited for explicitly with wait_vm).
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+__device__ __forceinline__ bf16x8 ld16(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+// Make the compiler complete a register load here, before the tile copies
+// that follow are issued: its own waits count only its own loads, so a wait
+// for this value inside the tile loop would also drain the copies.
+__device__ __forceinline__ void settle(const bf16x8& x) { asm volatile("" ::"v"(__builtin_bit_cast(u32x4, x))); }
+__device__ __forceinline__ void settle(float x) { asm volatile("" ::"v"(x)); }
+
+// Swizzle of a row-major LDS tile with CPR 16-byte chunks per row: logical
+// chunk c of row r is stored at chunk r*CPR + (c ^ swz<CPR>(r)).  For every
+// CPR, 16 consecutive rows read at one logical chunk hit 16 different
+// 16-byte bank groups, so a 16-byte read of 32 rows has no bank conflict.
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+  static_assert(CPR == 4 || CPR == 8 || CPR == 16, "chunks per row");
+  if constexpr (CPR == 16) return r & 15;
+  else if constexpr (CPR == 8) return (r >> 1) & 7;
+  else return (r >> 2) & 3;
+}
+
+// Row of a 16-row group that the transposed copies store at position p
+// (0..15).  An MFMA accumulator gives lane half h the rows 4h..4h+3 and
+// 8+4h..8+4h+3 of each 16-row group, and an operand read takes 8 consecutive
+// positions, so position 8h+e holds row (e < 4 ? 4h+e : 8+4h+e-4).
+__device__ __forceinline__ int group_row(int p) {
+  const int h = (p >> 3) & 1, e = p & 7;
+  return (e < 4) ? 4 * h + e : 8 + 4 * h + (e - 4);
+}
 
 struct BwdArgs {
   const __bf16* q;
   const __bf16* k;
   const __bf16* v;
   const __bf16* dout;
-  const float* lse;
-  const float* dsum;  // D = rowsum(dO o O)   [BH][Tq]
-  float* dq_acc;      // fp32 dQ / scale      [BH][Tq][D]
+  const float* stats;  // [BH][nqb32][64]: lse2 x32, D x32 per 32-row block
+  const __bf16* qt;    // [BH][D][Tq_pad]
+  const __bf16* dot;   // [BH][D][Tq_pad]
+  const __bf16* kt;    // [BH][D][Tk_pad]
+  __bf16* dq;
   __bf16* dk;
   __bf16* dv;
-  int BH, Tq, Tk, num_kblocks;
+  int BH, Tq, Tk, Tq_pad, Tk_pad, nqb32;
   float scale, scale_log2;
 };
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
-  using C = BwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 Qs[kBQ * C::STR];
-  __shared__ __attribute__((aligned(16))) __bf16 dOs[kBQ * C::STR];
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[kBK * C::STR];
-  __shared__ __attribute__((aligned(16))) __bf16 dSt[kBK * C::STRS];
-  __shared__ float lse2s[kBQ];
-  __shared__ float Dss[kBQ];
-
-  const int tid = threadIdx.x;
-  const int wave = tid / 64, lane = tid % 64;
-  const int lr = lane % 32, hf = lane / 32;
-  const int g16 = lane % 16, csub = (lane / 16) % 2;
-  const int n_items = a.BH * a.num_kblocks;
-  const int item = xcd_remap(blockIdx.x, n_items);
-  const int kb = item % a.num_kblocks;  // key block 0 (most causal work) first within a head
-  const int bh = item / a.num_kblocks;
-  const int k0 = kb * kBK;
-  const int key = k0 + wave * 32 + lr;  // this lane's key (N index of S, dP)
-
-  const __bf16* Qh = a.q + (size_t)bh * a.Tq * D;
-  const __bf16* dOh = a.dout + (size_t)bh * a.Tq * D;
-  const __bf16* Kh = a.k + (size_t)bh * a.Tk * D;
-  const __bf16* Vh = a.v + (size_t)bh * a.Tk * D;
-  const float* lseh = a.lse + (size_t)bh * a.Tq;
-  const float* Dh = a.dsum + (size_t)bh * a.Tq;
-  float* dQh = a.dq_acc + (size_t)bh * a.Tq * D;
-
-  // K and V rows of this lane's key as B operands (lane holds row[16ks + 8hf + 0..7])
-  bf16x8 kf[C::KS], vf[C::KS];
-  {
-    const bool ok = key < a.Tk;
+// ---------------------------------------------------------------------------------
+// bwd_stats: 16 lanes per query row (padded to a multiple of 32 rows per head).
+template <int D>
+__global__ __launch_bounds__(256) void bwd_stats_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ dout,
+                                                        const float* __restrict__ lse, float* __restrict__ stats,
+                                                        int BH, int Tq, int nqb32) {
+  constexpr int PER = D / 16;
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  const int row = t / 16, sub = t % 16;
+  const int rows_pad = nqb32 * 32;
+  const int bh = row / rows_pad, qi = row % rows_pad;
+  const bool in_grid = bh < BH;
+  const bool ok = in_grid && qi < Tq;
+  float acc = 0.f;
+  if (ok) {
+    const size_t base = ((size_t)bh * Tq + qi) * D + sub * PER;
+    const uint16_t* op = reinterpret_cast<const uint16_t*>(o) + base;
+    const uint16_t* dp = reinterpret_cast<const uint16_t*>(dout) + base;
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      kf[ks] = __builtin_bit_cast(bf16x8, ok ? *reinterpret_cast<const u32x4*>(Kh + (size_t)key * D + 16 * ks + 8 * hf) : z);
-      vf[ks] = __builtin_bit_cast(bf16x8, ok ? *reinterpret_cast<const u32x4*>(Vh + (size_t)key * D + 16 * ks + 8 * hf) : z);
-    }
+    for (int j = 0; j < PER; ++j) acc += bf16_to_f32(op[j]) * bf16_to_f32(dp[j]);
   }
-  // the workgroup's 128 K rows in LDS (B operand of dQ = dS K, read transposed)
-  {
-    constexpr int CPR = D / 8;
 #pragma unroll
-    for (int i = 0; i < C::KPER; ++i) {
-      const int c = tid + i * kBwdThreads;
-      const int r = c / CPR, col = (c % CPR) * 8;
-      const int kk = k0 + r;
-      u32x4 t = {0u, 0u, 0u, 0u};
-      if (kk < a.Tk) t = *reinterpret_cast<const u32x4*>(Kh + (size_t)kk * D + col);
-      *reinterpret_cast<u32x4*>(Ks + r * C::STR + col) = t;
+  for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
+  if (in_grid && sub == 0) {
+    float l2 = INFINITY;
+    if (ok) {
+      const float l = lse[(size_t)bh * Tq + qi];
+      l2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
     }
+    float* blk = stats + ((size_t)bh * nqb32 + qi / 32) * 64;
+    blk[qi % 32] = l2;
+    blk[32 + qi % 32] = ok ? acc : 0.f;
   }
+}
 
-  f32x16 dKt[C::CB], dVt[C::CB];
-#pragma unroll
-  for (int cb = 0; cb < C::CB; ++cb) {
-    dKt[cb] = f32x16{};
-    dVt[cb] = f32x16{};
-  }
+// bwd_transpose: one 64-row block of one (tensor, head) per workgroup.
+// out[bh][c][tpos] = in[bh][t][c] with t = 16*(tpos/16) + group_row(tpos%16),
+// zero for t >= T.
+struct TransposeArgs {
+  const __bf16* in[3];
+  __bf16* out[3];
+  int T[3];
+  int Tpad[3];
+};
 
-  const int num_qt = (a.Tq + kBQ - 1) / kBQ;
-  const int qt_begin = CAUSAL ? min(k0 / kBQ, num_qt) : 0;
-
-  // stage one query tile (Q, dO rows and their LSE, D) into LDS
-  auto load_qtile = [&](int q0, u32x4 (&qr)[C::QPER], u32x4 (&dr)[C::QPER], float& lv, float& dvv) {
-    constexpr int CPR = D / 8;
-#pragma unroll
-    for (int i = 0; i < C::QPER; ++i) {
-      const int c = tid + i * kBwdThreads;
-      const int r = c / CPR, col = (c % CPR) * 8;
-      const int qq = q0 + r;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      qr[i] = qq < a.Tq ? *reinterpret_cast<const u32x4*>(Qh + (size_t)qq * D + col) : z;
-      dr[i] = qq < a.Tq ? *reinterpret_cast<const u32x4*>(dOh + (size_t)qq * D + col) : z;
-    }
-    if (tid < kBQ) {
-      const int qq = q0 + tid;
-      const float l = qq < a.Tq ? lseh[qq] : -INFINITY;
-      // rows past Tq or with no allowed key get P = 0 through LSE = +inf
-      lv = (l == -INFINITY) ? INFINITY : l * kLog2e;
-      dvv = qq < a.Tq ? Dh[qq] : 0.f;
-    }
-  };
-  auto store_qtile = [&](const u32x4 (&qr)[C::QPER], const u32x4 (&dr)[C::QPER], float lv, float dvv) {
-    constexpr int CPR = D / 8;
-#pragma unroll
-    for (int i = 0; i < C::QPER; ++i) {
-      const int c = tid + i * kBwdThreads;
-      const int r = c / CPR, col = (c % CPR) * 8;
-      *reinterpret_cast<u32x4*>(Qs + r * C::STR + col) = qr[i];
-      *reinterpret_cast<u32x4*>(dOs + r * C::STR + col) = dr[i];
-    }
-    if (tid < kBQ) {
-      lse2s[tid] = lv;
-      Dss[tid] = dvv;
-    }
-  };
-
-  u32x4 qr[C::QPER], dr[C::QPER];
-  float lv = 0.f, dvv = 0.f;
-  if (qt_begin < num_qt) {
-    load_qtile(qt_begin * kBQ, qr, dr, lv, dvv);
-    store_qtile(qr, dr, lv, dvv);
+template <int D>
+__global__ __launch_bounds__(256) void bwd_transpose_kernel(TransposeArgs a) {
+  constexpr int STR = D + 8;
+  constexpr int CPR = D / 8;
+  __shared__ __attribute__((aligned(16))) __bf16 tile[64 * STR];
+  const int which = blockIdx.z;
+  const int bh = blockIdx.y;
+  const int t0 = blockIdx.x * 64;
+  const int T = a.T[which], Tpad = a.Tpad[which];
+  if (t0 >= Tpad) return;
+  const __bf16* in = a.in[which] + (size_t)bh * T * D;
+  __bf16* out = a.out[which] + (size_t)bh * D * Tpad;
+  for (int c = threadIdx.x; c < 64 * CPR; c += 256) {
+    const int r = c / CPR, col = (c % CPR) * 8;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (t0 + r < T) x = *reinterpret_cast<const u32x4*>(in + (size_t)(t0 + r) * D + col);
+    *reinterpret_cast<u32x4*>(tile + r * STR + col) = x;
   }
   __syncthreads();
-
-  for (int qt = qt_begin; qt < num_qt; ++qt) {
-    const int q0 = qt * kBQ;
-    const bool more = qt + 1 < num_qt;
-    if (more) load_qtile(q0 + kBQ, qr, dr, lv, dvv);
-
-    // ---- S = Q K^T and dP = dO V^T (queries on M, this wave's keys on N) ----
-    f32x16 s[2], dp[2];
+  const uint16_t* ts = reinterpret_cast<const uint16_t*>(tile);
+  for (int it = threadIdx.x; it < D * 8; it += 256) {
+    const int c = it / 8, m = it % 8;  // output row c, positions 8m..8m+7
+    unsigned w[4];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      s[qb] = f32x16{};
-      dp[qb] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qs + (32 * qb + lr) * C::STR + 16 * ks + 8 * hf);
-        s[qb] = mfma32(qa, kf[ks], s[qb]);
-      }
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        const bf16x8 da = *reinterpret_cast<const bf16x8*>(dOs + (32 * qb + lr) * C::STR + 16 * ks + 8 * hf);
-        dp[qb] = mfma32(da, vf[ks], dp[qb]);
-      }
+    for (int e = 0; e < 8; e += 2) {
+      const int p0 = 8 * m + e, p1 = p0 + 1;
+      const int r0 = (p0 & ~15) + group_row(p0 & 15), r1 = (p1 & ~15) + group_row(p1 & 15);
+      w[e / 2] = (unsigned)ts[r0 * STR + c] | ((unsigned)ts[r1 * STR + c] << 16);
     }
-    // ---- P = exp(S - LSE), dS = P o (dP - D) -------------------------------------
-    const bool need_mask = (k0 + wave * 32 + 32 > a.Tk) || (CAUSAL && q0 < k0 + wave * 32 + 31);
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int qi = 32 * qb + 8 * g + 4 * hf;  // first of 4 consecutive local queries
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + qi);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(Dss + qi);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = 4 * g + j;
-          float p = fast_exp2(__builtin_fmaf(s[qb][r], a.scale_log2, -l4[j]));
-          if (need_mask) {
-            const bool blocked = key >= a.Tk || (CAUSAL && key > q0 + qi + j);
-            p = blocked ? 0.f : p;
-          }
-          s[qb][r] = p;
-          dp[qb][r] = p * (dp[qb][r] - d4[j]);
-        }
-      }
-    // k-slot 8*hf+e of (qb,u) <-> local query 32*qb + 16*u + (e<4 ? 4*hf+e : 8+4*hf+e-4)
-    bf16x8 pb[2][2], sb[2][2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pb[qb][u][e] = to_bf16(s[qb][8 * u + e]);
-          sb[qb][u][e] = to_bf16(dp[qb][8 * u + e]);
-        }
-    // ---- dV^T += dO^T P and dK^T += Q^T dS --------------------------------------
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int r0 = 32 * qb + 16 * u + 4 * hf + g16 / 4;
-#pragma unroll
-        for (int cb = 0; cb < C::CB; ++cb) {
-          const int c0 = 32 * cb + 16 * csub + 4 * (g16 % 4);
-          const i16x4 dlo = lds_read_tr(dOs + r0 * C::STR + c0);
-          const i16x4 dhi = lds_read_tr(dOs + (r0 + 8) * C::STR + c0);
-          dVt[cb] = mfma32(join_tr(dlo, dhi), pb[qb][u], dVt[cb]);
-          const i16x4 qlo = lds_read_tr(Qs + r0 * C::STR + c0);
-          const i16x4 qhi = lds_read_tr(Qs + (r0 + 8) * C::STR + c0);
-          dKt[cb] = mfma32(join_tr(qlo, qhi), sb[qb][u], dKt[cb]);
-        }
-      }
-    // ---- dS^T (bf16) to LDS: row = key, 4 consecutive queries per 8-byte write ---
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 w = {pack_bf16x2(dp[qb][4 * g], dp[qb][4 * g + 1]), pack_bf16x2(dp[qb][4 * g + 2], dp[qb][4 * g + 3])};
-        *reinterpret_cast<u32x2*>(dSt + (wave * 32 + lr) * C::STRS + 32 * qb + 8 * g + 4 * hf) = w;
-      }
-    __syncthreads();
+    const u32x4 v = {w[0], w[1], w[2], w[3]};
+    *reinterpret_cast<u32x4*>(out + (size_t)c * Tpad + t0 + 8 * m) = v;
+  }
+}
 
-    // ---- dQ_tile += dS K over the workgroup's 128 keys (fp32 atomics) -----------
+// ---------------------------------------------------------------------------------
+// bwd_dkdv
+template <int D>
+struct KvCfg {
+  static constexpr int KS = D / 16;    // 16-wide k-steps over d
+  static constexpr int CB = D / 32;    // 32-row blocks of d
+  static constexpr int CPR = D / 8;    // 16-byte chunks per Q / dO row
+  static constexpr int WAVES = 4;
+  static constexpr int BK = 32 * WAVES;                // keys per workgroup
+  static constexpr int TILE = 32 * D;                  // bf16 elements of one Q, dO, Q^T or dO^T tile
+  static constexpr int DMA = TILE * 2 / 1024 / WAVES;  // wave copies per tensor and tile
+  static constexpr int VM = 4 * DMA + 1;               // vector-memory ops per wave and tile (+ stats)
+  static constexpr int STAGE = 4 * TILE + 128;         // bf16 elements per stage (stats: 64 floats)
+  static_assert(DMA >= 1 && TILE * 2 == DMA * WAVES * 1024, "tile copy split");
+};
+
+struct KvWave {
+  bf16x8 kf[8], vf[8];  // K, V rows of this lane's key as B operands
+  f32x16 dkt[4], dvt[4];
+};
+
+template <int D>
+__device__ __forceinline__ void dkdv_issue(const BwdArgs& a, int bh, int t, __bf16* stg, int wave, int lane) {
+  using C = KvCfg<D>;
+  const __bf16* Qh = a.q + (size_t)bh * a.Tq * D;
+  const __bf16* dOh = a.dout + (size_t)bh * a.Tq * D;
+  const __bf16* QTh = a.qt + (size_t)bh * D * a.Tq_pad;
+  const __bf16* dOTh = a.dot + (size_t)bh * D * a.Tq_pad;
 #pragma unroll
-    for (int ob = 0; ob < C::QBLK_PER_WAVE; ++ob) {
-      const int blk = wave * C::QBLK_PER_WAVE + ob;
-      const int qb = blk / C::CB, cb = blk % C::CB;
-      f32x16 acc = f32x16{};
+  for (int n = 0; n < C::DMA; ++n) {
+    const int i = wave * C::DMA + n;
+    const int p = 64 * i + lane;
+    const int row = p / C::CPR, c = (p % C::CPR) ^ swz<C::CPR>(row);
+    const int qq = min(32 * t + row, a.Tq - 1);
+    dma16(Qh + (size_t)qq * D + 8 * c, stg + 512 * i);
+    dma16(dOh + (size_t)qq * D + 8 * c, stg + C::TILE + 512 * i);
+    const int rt = p / 4, ct = (p % 4) ^ swz<4>(rt);
+    dma16(QTh + (size_t)rt * a.Tq_pad + 32 * t + 8 * ct, stg + 2 * C::TILE + 512 * i);
+    dma16(dOTh + (size_t)rt * a.Tq_pad + 32 * t + 8 * ct, stg + 3 * C::TILE + 512 * i);
+  }
+  // 256 bytes of row statistics: lanes 0..3 of every wave copy 64 of them
+  if (lane < 4) {
+    const float* src = a.stats + ((size_t)bh * a.nqb32 + t) * 64 + 16 * wave + 4 * lane;
+    dma16(reinterpret_cast<const __bf16*>(src), stg + 4 * C::TILE + 32 * wave);
+  }
+}
+
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void dkdv_compute(const BwdArgs& a, KvWave& w, const __bf16* stg, int t, int kw, int lane) {
+  using C = KvCfg<D>;
+  const int lr = lane % 32, hf = lane / 32;
+  const int key = kw + lr;
+  const __bf16* Qs = stg;
+  const __bf16* dOs = stg + C::TILE;
+  const __bf16* QTs = stg + 2 * C::TILE;
+  const __bf16* dOTs = stg + 3 * C::TILE;
+  const float* sts = reinterpret_cast<const float*>(stg + 4 * C::TILE);
+  const int rsw = swz<C::CPR>(lr);
+  f32x16 s = {}, dp = {};
 #pragma unroll
-      for (int ks = 0; ks < kBK / 16; ++ks) {
-        const int rr = 16 * ks + 8 * hf + g16 / 4;
-        const i16x4 alo = lds_read_tr(dSt + rr * C::STRS + 32 * qb + 16 * csub + 4 * (g16 % 4));
-        const i16x4 ahi = lds_read_tr(dSt + (rr + 4) * C::STRS + 32 * qb + 16 * csub + 4 * (g16 % 4));
-        const i16x4 blo = lds_read_tr(Ks + rr * C::STR + 32 * cb + 16 * csub + 4 * (g16 % 4));
-        const i16x4 bhi = lds_read_tr(Ks + (rr + 4) * C::STR + 32 * cb + 16 * csub + 4 * (g16 % 4));
-        acc = mfma32(join_tr(alo, ahi), join_tr(blo, bhi), acc);
-      }
+  for (int ks = 0; ks < C::KS; ++ks) s = mfma32(ld16(Qs + lr * D + 8 * ((2 * ks + hf) ^ rsw)), w.kf[ks], s);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qq = q0 + 32 * qb + 8 * (r / 4) + 4 * hf + (r % 4);
-        if (qq < a.Tq) unsafeAtomicAdd(dQh + (size_t)qq * D + 32 * cb + lr, acc[r]);
-      }
+  for (int ks = 0; ks < C::KS; ++ks) dp = mfma32(ld16(dOs + lr * D + 8 * ((2 * ks + hf) ^ rsw)), w.vf[ks], dp);
+  // accumulator register r: query 32t + 8(r/4) + 4hf + r%4, key `key`
+  const bool need_mask = CAUSAL && 32 * t < kw + 31;
+  bf16x8 pb[2], db[2];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const f32x4 l4 = *reinterpret_cast<const f32x4*>(sts + 8 * g + 4 * hf);
+    const f32x4 d4 = *reinterpret_cast<const f32x4*>(sts + 32 + 8 * g + 4 * hf);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * g + i;
+      float p = fast_exp2(__builtin_fmaf(s[r], a.scale_log2, -l4[i]));
+      if (need_mask) p = (key > 32 * t + 8 * g + 4 * hf + i) ? 0.f : p;
+      pb[r / 8][r % 8] = to_bf16(p);
+      db[r / 8][r % 8] = to_bf16(p * (dp[r] - d4[i]));
     }
+  }
+  const int tsw = swz<4>(lr);
+#pragma unroll
+  for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int off = (32 * cb + lr) * 32 + 8 * ((2 * s2 + hf) ^ tsw);
+      w.dvt[cb] = mfma32(ld16(dOTs + off), pb[s2], w.dvt[cb]);
+      w.dkt[cb] = mfma32(ld16(QTs + off), db[s2], w.dkt[cb]);
+    }
+}
 
-    if (more) store_qtile(qr, dr, lv, dvv);
-    __syncthreads();
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
+  using C = KvCfg<D>;
+  __shared__ __attribute__((aligned(1024))) __bf16 stg0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 stg1[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 stg2[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 stg3[C::STAGE];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
+  const int lr = lane % 32, hf = lane / 32;
+  const int nkb = (a.Tk + C::BK - 1) / C::BK;
+  const int item = xcd_remap(blockIdx.x, a.BH * nkb);
+  const int kb = item % nkb;  // lowest key block (most causal work) first within a head
+  const int bh = item / nkb;
+  const int k0 = kb * C::BK;
+  const int kw = k0 + 32 * wave;
+  const int key = kw + lr;
+
+  KvWave w;
+  {
+    const __bf16* Kh = a.k + (size_t)bh * a.Tk * D;
+    const __bf16* Vh = a.v + (size_t)bh * a.Tk * D;
+    const int kr = min(key, a.Tk - 1);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      w.kf[ks] = ld16(Kh + (size_t)kr * D + 16 * ks + 8 * hf);
+      w.vf[ks] = ld16(Vh + (size_t)kr * D + 16 * ks + 8 * hf);
+    }
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb) {
+      w.dkt[cb] = f32x16{};
+      w.dvt[cb] = f32x16{};
+    }
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      settle(w.kf[ks]);
+      settle(w.vf[ks]);
+    }
   }
 
-  // ---- dK = scale * dK^T^T, dV: lane holds key row, 4 consecutive columns per group
+  const int nqt = (a.Tq + 31) / 32;
+  const int t_begin = CAUSAL ? min(k0 / 32, nqt) : 0;
+  const int n = nqt - t_begin;
+  const bool wave_active = kw < a.Tk;
+
+  // tiles 0..2 in flight before the loop; tile j+3 is issued at step j
+  if (n > 0) dkdv_issue<D>(a, bh, t_begin, stg0, wave, lane);
+  if (n > 1) dkdv_issue<D>(a, bh, t_begin + 1, stg1, wave, lane);
+  if (n > 2) dkdv_issue<D>(a, bh, t_begin + 2, stg2, wave, lane);
+
+  auto step = [&](int j, const __bf16* cur, __bf16* ahead) {
+    // tile j has landed once at most the copies of tiles j+1, j+2 are pending
+    const int after = min(2, n - 1 - j);
+    if (after >= 2) wait_vm<2 * C::VM>();
+    else if (after == 1) wait_vm<C::VM>();
+    else wait_vm<0>();
+    barrier();
+    if (j + 3 < n) dkdv_issue<D>(a, bh, t_begin + j + 3, ahead, wave, lane);
+    const int t = t_begin + j;
+    // skipped when every query of the tile precedes every key of the wave
+    if (wave_active && !(CAUSAL && 32 * t + 31 < kw)) dkdv_compute<D, CAUSAL>(a, w, cur, t, kw, lane);
+  };
+  for (int j = 0; j < n; j += 4) {
+    step(j, stg0, stg3);
+    if (j + 1 < n) step(j + 1, stg1, stg0);
+    if (j + 2 < n) step(j + 2, stg2, stg1);
+    if (j + 3 < n) step(j + 3, stg3, stg2);
+  }
+
+  // dK = scale * (dK^T)^T, dV: register r of block cb is column 32cb + 8(r/4) + 4hf + r%4
   if (key < a.Tk) {
     __bf16* dkr = a.dk + ((size_t)bh * a.Tk + key) * D;
     __bf16* dvr = a.dv + ((size_t)bh * a.Tk + key) * D;
@@ -288,109 +356,279 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_bf16_kernel(BwdArgs a) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int c = 32 * cb + 8 * g + 4 * hf;
-        u32x2 wk = {pack_bf16x2(dKt[cb][4 * g] * a.scale, dKt[cb][4 * g + 1] * a.scale),
-                    pack_bf16x2(dKt[cb][4 * g + 2] * a.scale, dKt[cb][4 * g + 3] * a.scale)};
-        u32x2 wv = {pack_bf16x2(dVt[cb][4 * g], dVt[cb][4 * g + 1]),
-                    pack_bf16x2(dVt[cb][4 * g + 2], dVt[cb][4 * g + 3])};
+        const u32x2 wk = {pack_bf16x2(w.dkt[cb][4 * g] * a.scale, w.dkt[cb][4 * g + 1] * a.scale),
+                          pack_bf16x2(w.dkt[cb][4 * g + 2] * a.scale, w.dkt[cb][4 * g + 3] * a.scale)};
+        const u32x2 wv = {pack_bf16x2(w.dvt[cb][4 * g], w.dvt[cb][4 * g + 1]),
+                          pack_bf16x2(w.dvt[cb][4 * g + 2], w.dvt[cb][4 * g + 3])};
         *reinterpret_cast<u32x2*>(dkr + c) = wk;
         *reinterpret_cast<u32x2*>(dvr + c) = wv;
       }
   }
 }
 
-// D_i = sum_c dO_ic O_ic in fp32 and zero the fp32 dQ workspace row.
-// 16 lanes per row, D/16 elements per lane.
+// ---------------------------------------------------------------------------------
+// bwd_dq
 template <int D>
-__global__ __launch_bounds__(256) void bwd_preprocess_kernel(const __bf16* __restrict__ o,
-                                                             const __bf16* __restrict__ dout,
-                                                             float* __restrict__ dsum, float* __restrict__ dq_acc,
-                                                             int rows) {
-  constexpr int PER = D / 16;
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  const int row = t / 16, sub = t % 16;
-  const bool ok = row < rows;
-  float acc = 0.f;
-  if (ok) {
-    const uint16_t* op = reinterpret_cast<const uint16_t*>(o) + (size_t)row * D + sub * PER;
-    const uint16_t* dp = reinterpret_cast<const uint16_t*>(dout) + (size_t)row * D + sub * PER;
+struct DqCfg {
+  static constexpr int KS = D / 16;
+  static constexpr int CB = D / 32;
+  static constexpr int CPR = D / 8;                    // 16-byte chunks per K / V row
+  static constexpr int WAVES = 8;
+  static constexpr int BM = 32 * WAVES;                // queries per workgroup
+  static constexpr int TILE = 64 * D;                  // bf16 elements of one K, V or K^T tile
+  static constexpr int DMA = TILE * 2 / 1024 / WAVES;  // wave copies per tensor and tile
+  static constexpr int VM = 3 * DMA;
+  static constexpr int STAGE = 3 * TILE;
+  static_assert(DMA >= 1 && TILE * 2 == DMA * WAVES * 1024, "tile copy split");
+};
+
+struct DqWave {
+  bf16x8 qf[8], df[8];  // Q, dO rows of this lane's query as B operands
+  f32x16 dqt[4];
+  float lse2, dsum;
+};
+
+template <int D>
+__device__ __forceinline__ void dq_issue(const BwdArgs& a, int bh, int j, __bf16* stg, int wave, int lane) {
+  using C = DqCfg<D>;
+  const __bf16* Kh = a.k + (size_t)bh * a.Tk * D;
+  const __bf16* Vh = a.v + (size_t)bh * a.Tk * D;
+  const __bf16* KTh = a.kt + (size_t)bh * D * a.Tk_pad;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) acc += bf16_to_f32(op[j]) * bf16_to_f32(dp[j]);
-    float* z = dq_acc + (size_t)row * D + sub * PER;
-#pragma unroll
-    for (int j = 0; j < PER; j += 4) *reinterpret_cast<f32x4*>(z + j) = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int n = 0; n < C::DMA; ++n) {
+    const int i = wave * C::DMA + n;
+    const int p = 64 * i + lane;
+    const int row = p / C::CPR, c = (p % C::CPR) ^ swz<C::CPR>(row);
+    const int kk = min(64 * j + row, a.Tk - 1);
+    dma16(Kh + (size_t)kk * D + 8 * c, stg + 512 * i);
+    dma16(Vh + (size_t)kk * D + 8 * c, stg + C::TILE + 512 * i);
+    const int rt = p / 8, ct = (p % 8) ^ swz<8>(rt);
+    dma16(KTh + (size_t)rt * a.Tk_pad + 64 * j + 8 * ct, stg + 2 * C::TILE + 512 * i);
   }
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
-  if (ok && sub == 0) dsum[row] = acc;
 }
 
-// dQ = scale * dq_acc rounded to bf16, 8 elements per thread.
-__global__ __launch_bounds__(256) void bwd_finalize_kernel(const float* __restrict__ dq_acc, __bf16* __restrict__ dq,
-                                                           float scale, size_t n8) {
-  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n8) return;
-  const f32x4 x0 = *reinterpret_cast<const f32x4*>(dq_acc + i * 8);
-  const f32x4 x1 = *reinterpret_cast<const f32x4*>(dq_acc + i * 8 + 4);
-  u32x4 w = {pack_bf16x2(x0[0] * scale, x0[1] * scale), pack_bf16x2(x0[2] * scale, x0[3] * scale),
-             pack_bf16x2(x1[0] * scale, x1[1] * scale), pack_bf16x2(x1[2] * scale, x1[3] * scale)};
-  *reinterpret_cast<u32x4*>(dq + i * 8) = w;
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void dq_compute(const BwdArgs& a, DqWave& w, const __bf16* stg, int j, int qw, int kend,
+                                           int lane) {
+  using C = DqCfg<D>;
+  const int lr = lane % 32, hf = lane / 32;
+  const int my_q = qw + lr;
+  const __bf16* Ks = stg;
+  const __bf16* Vs = stg + C::TILE;
+  const __bf16* KTs = stg + 2 * C::TILE;
+  const int rsw = swz<C::CPR>(lr);
+  const int tsw = swz<8>(lr);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int key0 = 64 * j + 32 * u;
+    if (key0 >= kend) break;
+    f32x16 st = {}, dpt = {};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+      st = mfma32(ld16(Ks + (32 * u + lr) * D + 8 * ((2 * ks + hf) ^ rsw)), w.qf[ks], st);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+      dpt = mfma32(ld16(Vs + (32 * u + lr) * D + 8 * ((2 * ks + hf) ^ rsw)), w.df[ks], dpt);
+    // accumulator register r: key key0 + 8(r/4) + 4hf + r%4, query my_q
+    const bool need_mask = (CAUSAL && key0 + 31 > qw) || key0 + 32 > a.Tk;
+    bf16x8 db[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float p = fast_exp2(__builtin_fmaf(st[r], a.scale_log2, -w.lse2));
+      if (need_mask) {
+        const int kk = key0 + 8 * (r / 4) + 4 * hf + (r % 4);
+        p = ((CAUSAL && kk > my_q) || kk >= a.Tk) ? 0.f : p;
+      }
+      db[r / 8][r % 8] = to_bf16(p * (dpt[r] - w.dsum));
+    }
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+        w.dqt[cb] = mfma32(ld16(KTs + (32 * cb + lr) * 64 + 8 * ((4 * u + 2 * s2 + hf) ^ tsw)), db[s2], w.dqt[cb]);
+  }
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a) {
+  using C = DqCfg<D>;
+  __shared__ __attribute__((aligned(1024))) __bf16 stg0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 stg1[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 stg2[C::STAGE];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
+  const int lr = lane % 32, hf = lane / 32;
+  const int nqb = (a.Tq + C::BM - 1) / C::BM;
+  const int item = xcd_remap(blockIdx.x, a.BH * nqb);
+  const int bh = item / nqb;
+  const int qb = CAUSAL ? nqb - 1 - item % nqb : item % nqb;  // most causal work first within a head
+  const int q0 = qb * C::BM;
+  const int qw = q0 + 32 * wave;
+  const int my_q = qw + lr;
+
+  DqWave w;
+  {
+    const __bf16* Qh = a.q + (size_t)bh * a.Tq * D;
+    const __bf16* dOh = a.dout + (size_t)bh * a.Tq * D;
+    const int qr = min(my_q, a.Tq - 1);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      w.qf[ks] = ld16(Qh + (size_t)qr * D + 16 * ks + 8 * hf);
+      w.df[ks] = ld16(dOh + (size_t)qr * D + 16 * ks + 8 * hf);
+    }
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb) w.dqt[cb] = f32x16{};
+    w.lse2 = INFINITY;
+    w.dsum = 0.f;
+    if (my_q < a.Tq) {
+      const float* blk = a.stats + ((size_t)bh * a.nqb32 + my_q / 32) * 64;
+      w.lse2 = blk[my_q % 32];
+      w.dsum = blk[32 + my_q % 32];
+    }
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      settle(w.qf[ks]);
+      settle(w.df[ks]);
+    }
+    settle(w.lse2);
+    settle(w.dsum);
+  }
+
+  const int nkt_all = (a.Tk + 63) / 64;
+  const int last_q = min(q0 + C::BM - 1, a.Tq - 1);
+  const int n = CAUSAL ? min(nkt_all, last_q / 64 + 1) : nkt_all;
+  // keys this wave needs: [0, kend)
+  const int kend = qw >= a.Tq ? 0 : (CAUSAL ? min(a.Tk, min(qw + 31, a.Tq - 1) + 1) : a.Tk);
+
+  // tiles 0, 1 in flight before the loop; tile j+2 is issued at step j
+  if (n > 0) dq_issue<D>(a, bh, 0, stg0, wave, lane);
+  if (n > 1) dq_issue<D>(a, bh, 1, stg1, wave, lane);
+
+  auto step = [&](int j, const __bf16* cur, __bf16* ahead) {
+    if (j + 1 < n) wait_vm<C::VM>();
+    else wait_vm<0>();
+    barrier();
+    if (j + 2 < n) dq_issue<D>(a, bh, j + 2, ahead, wave, lane);
+    if (64 * j < kend) dq_compute<D, CAUSAL>(a, w, cur, j, qw, kend, lane);
+  };
+  for (int j = 0; j < n; j += 3) {
+    step(j, stg0, stg2);
+    if (j + 1 < n) step(j + 1, stg1, stg0);
+    if (j + 2 < n) step(j + 2, stg2, stg1);
+  }
+
+  // dQ = scale * (dQ^T)^T: register r of block cb is column 32cb + 8(r/4) + 4hf + r%4
+  if (my_q < a.Tq) {
+    __bf16* dqr = a.dq + ((size_t)bh * a.Tq + my_q) * D;
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const u32x2 wq = {pack_bf16x2(w.dqt[cb][4 * g] * a.scale, w.dqt[cb][4 * g + 1] * a.scale),
+                          pack_bf16x2(w.dqt[cb][4 * g + 2] * a.scale, w.dqt[cb][4 * g + 3] * a.scale)};
+        *reinterpret_cast<u32x2*>(dqr + 32 * cb + 8 * g + 4 * hf) = wq;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+struct BwdLayout {
+  size_t stats, qt, dot, kt, total;
+};
+
+BwdLayout bwd_layout(int BH, int Tq, int Tk, int d) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t nqb32 = (size_t)(Tq + 31) / 32;
+  const size_t tq_pad = (size_t)(Tq + 63) / 64 * 64, tk_pad = (size_t)(Tk + 63) / 64 * 64;
+  BwdLayout L;
+  L.stats = 0;
+  L.qt = up(L.stats + (size_t)BH * nqb32 * 64 * sizeof(float));
+  L.dot = up(L.qt + (size_t)BH * d * tq_pad * 2);
+  L.kt = up(L.dot + (size_t)BH * d * tq_pad * 2);
+  L.total = up(L.kt + (size_t)BH * d * tk_pad * 2);
+  return L;
 }
 
 template <int D>
-hipError_t bwd_launch_d(const BwdArgs& args, const __bf16* o, __bf16* dq, bool causal, hipStream_t stream) {
-  const int rows = args.BH * args.Tq;
+hipError_t bwd_launch_d(BwdArgs& args, const __bf16* o, const float* lse, bool causal, char* ws,
+                        const BwdLayout& L, hipStream_t stream) {
+  // pre-pass: row statistics and transposed copies
   prof_begin(2, stream);
-  hipLaunchKernelGGL(bwd_preprocess_kernel<D>, dim3((rows * 16 + 255) / 256), dim3(256), 0, stream, o, args.dout,
-                     const_cast<float*>(args.dsum), args.dq_acc, rows);
+  {
+    const int rows = args.BH * args.nqb32 * 32;
+    hipLaunchKernelGGL(bwd_stats_kernel<D>, dim3((rows * 16 + 255) / 256), dim3(256), 0, stream, o, args.dout, lse,
+                       reinterpret_cast<float*>(ws + L.stats), args.BH, args.Tq, args.nqb32);
+    TransposeArgs t;
+    t.in[0] = args.q;
+    t.in[1] = args.dout;
+    t.in[2] = args.k;
+    t.out[0] = reinterpret_cast<__bf16*>(ws + L.qt);
+    t.out[1] = reinterpret_cast<__bf16*>(ws + L.dot);
+    t.out[2] = reinterpret_cast<__bf16*>(ws + L.kt);
+    t.T[0] = t.T[1] = args.Tq;
+    t.T[2] = args.Tk;
+    t.Tpad[0] = t.Tpad[1] = args.Tq_pad;
+    t.Tpad[2] = args.Tk_pad;
+    const int blocks = max(args.Tq_pad, args.Tk_pad) / 64;
+    hipLaunchKernelGGL(bwd_transpose_kernel<D>, dim3(blocks, args.BH, 3), dim3(256), 0, stream, t);
+  }
   prof_end(2, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int n = args.BH * args.num_kblocks;
+
+  const int nkb = (args.Tk + KvCfg<D>::BK - 1) / KvCfg<D>::BK;
   prof_begin(3, stream);
   if (causal)
-    hipLaunchKernelGGL((bwd_bf16_kernel<D, true>), dim3(n), dim3(kBwdThreads), 0, stream, args);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(args.BH * nkb), dim3(256), 0, stream, args);
   else
-    hipLaunchKernelGGL((bwd_bf16_kernel<D, false>), dim3(n), dim3(kBwdThreads), 0, stream, args);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(args.BH * nkb), dim3(256), 0, stream, args);
   prof_end(3, stream);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t n8 = (size_t)rows * D / 8;
+
+  const int nqb = (args.Tq + DqCfg<D>::BM - 1) / DqCfg<D>::BM;
   prof_begin(4, stream);
-  hipLaunchKernelGGL(bwd_finalize_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, args.dq_acc, dq,
-                     args.scale, n8);
+  if (causal)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3(args.BH * nqb), dim3(512), 0, stream, args);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3(args.BH * nqb), dim3(512), 0, stream, args);
   prof_end(4, stream);
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t bwd_bf16_workspace_bytes(int BH, int Tq, int d) {
-  return (size_t)BH * Tq * d * sizeof(float) + (size_t)BH * Tq * sizeof(float);
-}
+size_t bwd_bf16_workspace_bytes(int BH, int Tq, int Tk, int d) { return bwd_layout(BH, Tq, Tk, d).total; }
 
 hipError_t bwd_bf16_launch(const void* q, const void* k, const void* v, const void* o, const float* lse,
                            const void* dout, void* dq, void* dk, void* dv, int BH, int Tq, int Tk, int d,
                            float scale, int causal, void* workspace, hipStream_t stream) {
+  const BwdLayout L = bwd_layout(BH, Tq, Tk, d);
+  char* ws = static_cast<char*>(workspace);
   BwdArgs a;
   a.q = static_cast<const __bf16*>(q);
   a.k = static_cast<const __bf16*>(k);
   a.v = static_cast<const __bf16*>(v);
   a.dout = static_cast<const __bf16*>(dout);
-  a.lse = lse;
-  a.dq_acc = static_cast<float*>(workspace);
-  a.dsum = a.dq_acc + (size_t)BH * Tq * d;
+  a.stats = reinterpret_cast<const float*>(ws + L.stats);
+  a.qt = reinterpret_cast<const __bf16*>(ws + L.qt);
+  a.dot = reinterpret_cast<const __bf16*>(ws + L.dot);
+  a.kt = reinterpret_cast<const __bf16*>(ws + L.kt);
+  a.dq = static_cast<__bf16*>(dq);
   a.dk = static_cast<__bf16*>(dk);
   a.dv = static_cast<__bf16*>(dv);
   a.BH = BH;
   a.Tq = Tq;
   a.Tk = Tk;
-  a.num_kblocks = (Tk + kBK - 1) / kBK;
+  a.Tq_pad = (Tq + 63) / 64 * 64;
+  a.Tk_pad = (Tk + 63) / 64 * 64;
+  a.nqb32 = (Tq + 31) / 32;
   a.scale = scale;
   a.scale_log2 = scale * kLog2e;
   const __bf16* ob = static_cast<const __bf16*>(o);
-  __bf16* dqb = static_cast<__bf16*>(dq);
-  return d == 128 ? bwd_launch_d<128>(a, ob, dqb, causal != 0, stream)
-                  : bwd_launch_d<64>(a, ob, dqb, causal != 0, stream);
+  return d == 128 ? bwd_launch_d<128>(a, ob, lse, causal != 0, ws, L, stream)
+                  : bwd_launch_d<64>(a, ob, lse, causal != 0, ws, L, stream);
 }
 
 }  // namespace attn

@@ -107,8 +107,11 @@ int attn_fwd_splits(const void* q, const void* k, const void* v, void* o, float*
  *   dS  = P o (dout V^T - D)            ("attention backprop", "Gradient of S")
  *   dQ  = scale dS K,  dK = scale dS^T Q ("attention backprop", "Gradient of Q and K",
  *                                         with the chain-rule factor of `scale`)
- * dQ is summed over key blocks in an fp32 workspace (device atomics), so its
- * low bits may vary between runs; dK and dV are deterministic.
+ * dK, dV come from one kernel that walks the queries of each key block and
+ * dQ from another that walks the keys of each query block, so every output
+ * element is summed in a fixed order by one workgroup: results are
+ * deterministic.  Workspace (row statistics and transposed copies of Q, dO,
+ * K: about 3 * B*H*T*d*2 bytes) is allocated with hipMallocAsync on `stream`.
  * Supported: d == dv, d in {64, 128}; otherwise ATTN_ERR_UNSUPPORTED.
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -153,9 +156,9 @@ int attn_bwd_f32(const float* q, const float* k, const float* v, const float* o,
  */
 #define ATTN_KERNEL_FWD 0            /* forward main kernel */
 #define ATTN_KERNEL_FWD_COMBINE 1    /* merge of key-split partial states */
-#define ATTN_KERNEL_BWD_PREPROCESS 2 /* D = rowsum(dO o O), dQ workspace clear */
-#define ATTN_KERNEL_BWD 3            /* backward main kernel */
-#define ATTN_KERNEL_BWD_FINALIZE 4   /* dQ workspace -> bf16 */
+#define ATTN_KERNEL_BWD_PREP 2       /* D = rowsum(dO o O), LSE*log2(e), transposed Q, dO, K */
+#define ATTN_KERNEL_BWD_DKDV 3       /* backward: dK and dV */
+#define ATTN_KERNEL_BWD_DQ 4         /* backward: dQ */
 #define ATTN_KERNEL_KINDS 5
 int attn_profile_start(void);
 int attn_profile_stop(void);

@@ -176,17 +176,21 @@ def test_bf16_bwd_small(dev, shape, causal):
     assert_close("dV", f64(dv), rv, TOL_BF16)
 
 
-def test_bf16_inputs_unchanged_and_forward_deterministic(dev):
+def test_bf16_inputs_unchanged_and_results_deterministic(dev):
     q, k, v, do = bf16_problem((1, 2, 300, 333, 128, 128), seed=9)
     qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
     digest = lambda ts: [hashlib.sha256(t.view(torch.int16).cpu().numpy().tobytes()).hexdigest() for t in ts]
     before = digest((qd, kd, vd, dod))
     o1, l1 = attn.fwd(qd, kd, vd, causal=True)
     o2, l2 = attn.fwd(qd, kd, vd, causal=True)
-    attn.bwd(qd, kd, vd, o1, l1, dod, causal=True)
+    g1 = attn.bwd(qd, kd, vd, o1, l1, dod, causal=True)
+    g2 = attn.bwd(qd, kd, vd, o1, l1, dod, causal=True)
     torch.cuda.synchronize()
     assert digest((qd, kd, vd, dod)) == before
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+    # every gradient element is summed in a fixed order by one workgroup
+    for a, b in zip(g1, g2):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
 def test_bf16_scale_zero_gives_mean_of_allowed_values(dev):
