@@ -17,12 +17,11 @@
 //   bwd_stats      per query row: LSE * log2(e) (+inf for a row that is
 //                  outside Tq or has no allowed key, so its P is 0) and
 //                  D = sum_c dO_c O_c, blocked 32 rows at a time
-//   bwd_transpose  Q^T, dO^T, K^T ([d][T], T padded to 64 with zeros) into the
-//                  workspace, with the rows of every 16-row group in the
-//                  order the MFMA operands below take them
-//   bwd_dkdv       one workgroup (4 waves) per 128 keys; each wave keeps its
-//                  32 keys' K and V rows as MFMA operands and dK^T, dV^T in
-//                  registers and walks 32-query tiles streamed into LDS:
+//   bwd_transpose  K^T ([d][Tk], Tk padded to 64 with zeros) into the
+//                  workspace, with the keys of every 16-key group in the
+//                  order the dQ MFMA operand takes them
+//   bwd_dkdv       one workgroup (8 waves) per 128 keys, walking 32-query
+//                  tiles streamed into LDS (see the kernel's comment):
 //                    S = Q K^T, dP = dO V^T, P = exp2(S*scale*log2e - LSE2),
 //                    dS = P o (dP - D), dV^T += dO^T P, dK^T += Q^T dS
 //   bwd_dq         one workgroup (8 waves) per 256 queries; each wave keeps
@@ -30,9 +29,10 @@
 //                  registers and walks 64-key tiles streamed into LDS:
 //                    S^T = K Q^T, dP^T = V dO^T, dS^T as above,
 //                    dQ^T += K^T dS^T
-// Every LDS operand is read with 16-byte reads from a tile whose 16-byte
-// chunks are XOR-swizzled per row, and tiles are copied global -> LDS by the
-// direct-to-LDS vector load, several tiles ahead of the compute.
+// LDS tiles have their 16-byte chunks XOR-swizzled per row so that both
+// 16-byte row reads and transposing reads are free of bank conflicts, and
+// tiles are copied global -> LDS by the direct-to-LDS vector load, several
+// tiles ahead of the compute.
 #include "attn_common.hpp"
 #include "attn_launch.hpp"
 
@@ -59,9 +59,10 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-// Workgroup barrier that also keeps the compiler from moving memory accesses
-// across it (the tile copies are waited for explicitly with wait_vm).
-__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+// Workgroup barrier after this wave's LDS reads and writes have completed;
+// it also keeps the compiler from moving memory accesses across it.  Tile
+// copies into LDS are waited for separately (wait_vm) before it.
+__device__ __forceinline__ void barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 __device__ __forceinline__ bf16x8 ld16(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
@@ -74,12 +75,15 @@ __device__ __forceinline__ void settle(float x) { asm volatile("" ::"v"(x)); }
 // Swizzle of a row-major LDS tile with CPR 16-byte chunks per row: logical
 // chunk c of row r is stored at chunk r*CPR + (c ^ swz<CPR>(r)).  For every
 // CPR, 16 consecutive rows read at one logical chunk hit 16 different
-// 16-byte bank groups, so a 16-byte read of 32 rows has no bank conflict.
+// 16-byte bank groups (a 16-byte read of 32 rows has no bank conflict), and
+// for CPR 8 and 16 the 4 rows x 4 chunks that half a wave touches in a
+// transposing read (rows 4a..4a+3, chunks 4m..4m+3) are 16 different bank
+// groups as well.
 template <int CPR>
 __device__ __forceinline__ int swz(int r) {
   static_assert(CPR == 4 || CPR == 8 || CPR == 16, "chunks per row");
-  if constexpr (CPR == 16) return r & 15;
-  else if constexpr (CPR == 8) return (r >> 1) & 7;
+  if constexpr (CPR == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else if constexpr (CPR == 8) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
   else return (r >> 2) & 3;
 }
 
@@ -98,13 +102,11 @@ struct BwdArgs {
   const __bf16* v;
   const __bf16* dout;
   const float* stats;  // [BH][nqb32][64]: lse2 x32, D x32 per 32-row block
-  const __bf16* qt;    // [BH][D][Tq_pad]
-  const __bf16* dot;   // [BH][D][Tq_pad]
   const __bf16* kt;    // [BH][D][Tk_pad]
   __bf16* dq;
   __bf16* dk;
   __bf16* dv;
-  int BH, Tq, Tk, Tq_pad, Tk_pad, nqb32;
+  int BH, Tq, Tk, Tk_pad, nqb32;
   float scale, scale_log2;
 };
 
@@ -143,28 +145,19 @@ __global__ __launch_bounds__(256) void bwd_stats_kernel(const __bf16* __restrict
   }
 }
 
-// bwd_transpose: one 64-row block of one (tensor, head) per workgroup.
+// bwd_transpose: one 64-row block of one head per workgroup.
 // out[bh][c][tpos] = in[bh][t][c] with t = 16*(tpos/16) + group_row(tpos%16),
 // zero for t >= T.
-struct TransposeArgs {
-  const __bf16* in[3];
-  __bf16* out[3];
-  int T[3];
-  int Tpad[3];
-};
-
 template <int D>
-__global__ __launch_bounds__(256) void bwd_transpose_kernel(TransposeArgs a) {
+__global__ __launch_bounds__(256) void bwd_transpose_kernel(const __bf16* __restrict__ in_all,
+                                                            __bf16* __restrict__ out_all, int T, int Tpad) {
   constexpr int STR = D + 8;
   constexpr int CPR = D / 8;
   __shared__ __attribute__((aligned(16))) __bf16 tile[64 * STR];
-  const int which = blockIdx.z;
   const int bh = blockIdx.y;
   const int t0 = blockIdx.x * 64;
-  const int T = a.T[which], Tpad = a.Tpad[which];
-  if (t0 >= Tpad) return;
-  const __bf16* in = a.in[which] + (size_t)bh * T * D;
-  __bf16* out = a.out[which] + (size_t)bh * D * Tpad;
+  const __bf16* in = in_all + (size_t)bh * T * D;
+  __bf16* out = out_all + (size_t)bh * D * Tpad;
   for (int c = threadIdx.x; c < 64 * CPR; c += 256) {
     const int r = c / CPR, col = (c % CPR) * 8;
     u32x4 x = {0u, 0u, 0u, 0u};
@@ -188,24 +181,38 @@ __global__ __launch_bounds__(256) void bwd_transpose_kernel(TransposeArgs a) {
 }
 
 // ---------------------------------------------------------------------------------
-// bwd_dkdv
+// bwd_dkdv: one workgroup of 8 waves per 128 keys.  Waves w and w+4 run on the
+// same SIMD and share key group w (32 keys):
+//   score wave (w < 4): holds its keys' K and V rows as MFMA operands; per
+//     32-query tile computes S = Q K^T, dP = dO V^T, P and dS and hands P, dS
+//     (bf16 MFMA operands, in the lane layout both waves use) to its partner
+//     through LDS;
+//   gradient wave (w >= 4): holds dK^T, dV^T for one 32-column block of d
+//     and the key groups that go with it; one tile behind, adds dO^T P and
+//     Q^T dS, reading its column block of dO and Q with transposing LDS reads
+//     (shared by all its key groups) and P, dS from the score waves.
+// The partner's MFMA work fills the SIMD while the score wave does its
+// softmax, and neither role needs more than half the register file.
 template <int D>
 struct KvCfg {
-  static constexpr int KS = D / 16;    // 16-wide k-steps over d
-  static constexpr int CB = D / 32;    // 32-row blocks of d
-  static constexpr int CPR = D / 8;    // 16-byte chunks per Q / dO row
-  static constexpr int WAVES = 4;
-  static constexpr int BK = 32 * WAVES;                // keys per workgroup
-  static constexpr int TILE = 32 * D;                  // bf16 elements of one Q, dO, Q^T or dO^T tile
-  static constexpr int DMA = TILE * 2 / 1024 / WAVES;  // wave copies per tensor and tile
-  static constexpr int VM = 4 * DMA + 1;               // vector-memory ops per wave and tile (+ stats)
-  static constexpr int STAGE = 4 * TILE + 128;         // bf16 elements per stage (stats: 64 floats)
-  static_assert(DMA >= 1 && TILE * 2 == DMA * WAVES * 1024, "tile copy split");
-};
-
-struct KvWave {
-  bf16x8 kf[8], vf[8];  // K, V rows of this lane's key as B operands
-  f32x16 dkt[4], dvt[4];
+  static constexpr int KS = D / 16;                    // 16-wide k-steps over d
+  static constexpr int CB = D / 32;                    // 32-row blocks of d
+  static constexpr int CPR = D / 8;                    // 16-byte chunks per Q / dO row
+  static constexpr int WAVES = 8;
+  static constexpr int BK = 128;                       // keys per workgroup
+  static constexpr int TILE = 32 * D;                  // bf16 elements of one Q or dO tile
+  static constexpr int PER_TENSOR = TILE * 2 / 1024;   // wave copies per tensor and tile
+  static constexpr int PER_WAVE = 2 * PER_TENSOR / WAVES;
+  static constexpr int VM = PER_WAVE + 1;              // vector-memory ops per wave and tile (+ stats)
+  static constexpr int STAGE = 2 * TILE + 128;         // bf16 elements per stage (stats: 64 floats)
+  static constexpr int NSTAGE = 6;                     // tiles j-1 .. j+4 resident
+  static constexpr int AHEAD = NSTAGE - 2;             // copies in flight ahead of the score waves
+  static constexpr int HAND_GRP = 64 * 4 * 8;          // bf16 elements of one group's P/dS hand-off (64 lanes x 4 x 8)
+  static constexpr int HAND = 4 * HAND_GRP;            // all 4 key groups
+  // gradient wave gw (0..3) owns column block gw % CB of d and key groups
+  // kgroup(gw, 0..CB-1): the 4 * CB (block, group) pairs, CB per wave
+  __host__ __device__ static constexpr int kgroup(int gw, int i) { return gw / CB + (4 / CB) * i; }
+  static_assert(PER_WAVE >= 1 && 2 * PER_TENSOR == PER_WAVE * WAVES, "tile copy split");
 };
 
 template <int D>
@@ -213,77 +220,130 @@ __device__ __forceinline__ void dkdv_issue(const BwdArgs& a, int bh, int t, __bf
   using C = KvCfg<D>;
   const __bf16* Qh = a.q + (size_t)bh * a.Tq * D;
   const __bf16* dOh = a.dout + (size_t)bh * a.Tq * D;
-  const __bf16* QTh = a.qt + (size_t)bh * D * a.Tq_pad;
-  const __bf16* dOTh = a.dot + (size_t)bh * D * a.Tq_pad;
 #pragma unroll
-  for (int n = 0; n < C::DMA; ++n) {
-    const int i = wave * C::DMA + n;
+  for (int n = 0; n < C::PER_WAVE; ++n) {
+    const int cpy = wave * C::PER_WAVE + n;  // wave-uniform
+    const int tensor = cpy / C::PER_TENSOR, i = cpy % C::PER_TENSOR;
     const int p = 64 * i + lane;
     const int row = p / C::CPR, c = (p % C::CPR) ^ swz<C::CPR>(row);
     const int qq = min(32 * t + row, a.Tq - 1);
-    dma16(Qh + (size_t)qq * D + 8 * c, stg + 512 * i);
-    dma16(dOh + (size_t)qq * D + 8 * c, stg + C::TILE + 512 * i);
-    const int rt = p / 4, ct = (p % 4) ^ swz<4>(rt);
-    dma16(QTh + (size_t)rt * a.Tq_pad + 32 * t + 8 * ct, stg + 2 * C::TILE + 512 * i);
-    dma16(dOTh + (size_t)rt * a.Tq_pad + 32 * t + 8 * ct, stg + 3 * C::TILE + 512 * i);
+    dma16((tensor == 0 ? Qh : dOh) + (size_t)qq * D + 8 * c, stg + tensor * C::TILE + 512 * i);
   }
-  // 256 bytes of row statistics: lanes 0..3 of every wave copy 64 of them
-  if (lane < 4) {
-    const float* src = a.stats + ((size_t)bh * a.nqb32 + t) * 64 + 16 * wave + 4 * lane;
-    dma16(reinterpret_cast<const __bf16*>(src), stg + 4 * C::TILE + 32 * wave);
+  // 256 bytes of row statistics: lanes 0..1 of every wave copy 32 of them
+  if (lane < 2) {
+    const float* src = a.stats + ((size_t)bh * a.nqb32 + t) * 64 + 8 * wave + 4 * lane;
+    dma16(reinterpret_cast<const __bf16*>(src), stg + 2 * C::TILE + 16 * wave);
   }
 }
 
-template <int D, bool CAUSAL>
-__device__ __forceinline__ void dkdv_compute(const BwdArgs& a, KvWave& w, const __bf16* stg, int t, int kw, int lane) {
+// Score wave, one tile: P and dS as bf16 B operands (k-slot 8hf+e of k-step
+// s2 = accumulator register 8*s2 + e), stored per lane into `hand`.
+template <int D, bool MASK>
+__device__ __forceinline__ void dkdv_scores(const BwdArgs& a, const bf16x8 (&kf)[8], const bf16x8 (&vf)[8],
+                                            const __bf16* stg, __bf16* hand, int t, int kw, int lane) {
   using C = KvCfg<D>;
   const int lr = lane % 32, hf = lane / 32;
   const int key = kw + lr;
   const __bf16* Qs = stg;
   const __bf16* dOs = stg + C::TILE;
-  const __bf16* QTs = stg + 2 * C::TILE;
-  const __bf16* dOTs = stg + 3 * C::TILE;
-  const float* sts = reinterpret_cast<const float*>(stg + 4 * C::TILE);
+  const float* sts = reinterpret_cast<const float*>(stg + 2 * C::TILE);
   const int rsw = swz<C::CPR>(lr);
+  // every LDS read of the tile is issued before the first MFMA, so their
+  // latencies overlap instead of adding up
+  bf16x8 qa[C::KS], da[C::KS];
+  f32x4 l4[4], d4[4];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    const int off = lr * D + 8 * ((2 * ks + hf) ^ rsw);
+    qa[ks] = ld16(Qs + off);
+    da[ks] = ld16(dOs + off);
+  }
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    l4[g] = *reinterpret_cast<const f32x4*>(sts + 8 * g + 4 * hf);
+    d4[g] = *reinterpret_cast<const f32x4*>(sts + 32 + 8 * g + 4 * hf);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // the score wave goes first on the SIMD's matrix unit; its partner's MFMAs
+  // then run while it does the softmax
+  __builtin_amdgcn_s_setprio(2);
   f32x16 s = {}, dp = {};
 #pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) s = mfma32(ld16(Qs + lr * D + 8 * ((2 * ks + hf) ^ rsw)), w.kf[ks], s);
-#pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) dp = mfma32(ld16(dOs + lr * D + 8 * ((2 * ks + hf) ^ rsw)), w.vf[ks], dp);
+  for (int ks = 0; ks < C::KS; ++ks) {
+    s = mfma32(qa[ks], kf[ks], s);
+    dp = mfma32(da[ks], vf[ks], dp);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(0);
   // accumulator register r: query 32t + 8(r/4) + 4hf + r%4, key `key`
-  const bool need_mask = CAUSAL && 32 * t < kw + 31;
   bf16x8 pb[2], db[2];
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    const f32x4 l4 = *reinterpret_cast<const f32x4*>(sts + 8 * g + 4 * hf);
-    const f32x4 d4 = *reinterpret_cast<const f32x4*>(sts + 32 + 8 * g + 4 * hf);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * g + i;
-      float p = fast_exp2(__builtin_fmaf(s[r], a.scale_log2, -l4[i]));
-      if (need_mask) p = (key > 32 * t + 8 * g + 4 * hf + i) ? 0.f : p;
+      float p = fast_exp2(__builtin_fmaf(s[r], a.scale_log2, -l4[g][i]));
+      if (MASK) p = (key > 32 * t + 8 * g + 4 * hf + i) ? 0.f : p;
       pb[r / 8][r % 8] = to_bf16(p);
-      db[r / 8][r % 8] = to_bf16(p * (dp[r] - d4[i]));
+      db[r / 8][r % 8] = to_bf16(p * (dp[r] - d4[g][i]));
     }
   }
-  const int tsw = swz<4>(lr);
+  u32x4* h = reinterpret_cast<u32x4*>(hand) + lane;
+  h[0] = __builtin_bit_cast(u32x4, pb[0]);
+  h[64] = __builtin_bit_cast(u32x4, pb[1]);
+  h[128] = __builtin_bit_cast(u32x4, db[0]);
+  h[192] = __builtin_bit_cast(u32x4, db[1]);
+}
+
+// Gradient wave, one tile: dV^T += dO^T P, dK^T += Q^T dS for its column
+// block cb of d and its CB key groups (KvCfg::kgroup).  The A operand (column
+// d = 32cb + lane%32, k-slots = queries) comes from two transposing reads of
+// the row-major tile, rows 16*s2 + 4hf + 0..3 and 16*s2 + 8 + 4hf + 0..3 (the
+// query order of the P / dS k-slots), and serves every key group.
+template <int D>
+__device__ __forceinline__ void dkdv_grads(f32x16 (&dkt)[4], f32x16 (&dvt)[4], const __bf16* stg, const __bf16* hands,
+                                           int gw, int lane) {
+  using C = KvCfg<D>;
+  const int hf = lane / 32, g16 = lane % 16, csub = (lane / 16) % 2;
+  const int cb = gw % C::CB;
+  const __bf16* Qs = stg;
+  const __bf16* dOs = stg + C::TILE;
+  // element (r, c) of a row-major swizzled tile
+  auto at = [](int r, int c) { return r * D + 8 * ((c >> 3) ^ swz<C::CPR>(r)) + (c & 7); };
+  bf16x8 ao[2], aq[2];
 #pragma unroll
-  for (int cb = 0; cb < C::CB; ++cb)
+  for (int s2 = 0; s2 < 2; ++s2) {
+    const int r0 = 16 * s2 + 4 * hf + g16 / 4;
+    const int c0 = 32 * cb + 16 * csub + 4 * (g16 % 4);
+    ao[s2] = join_tr(lds_read_tr(dOs + at(r0, c0)), lds_read_tr(dOs + at(r0 + 8, c0)));
+    aq[s2] = join_tr(lds_read_tr(Qs + at(r0, c0)), lds_read_tr(Qs + at(r0 + 8, c0)));
+  }
+  u32x4 pb[C::CB][2], db[C::CB][2];
+#pragma unroll
+  for (int i = 0; i < C::CB; ++i) {
+    const u32x4* h = reinterpret_cast<const u32x4*>(hands + C::kgroup(gw, i) * C::HAND_GRP) + lane;
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
-      const int off = (32 * cb + lr) * 32 + 8 * ((2 * s2 + hf) ^ tsw);
-      w.dvt[cb] = mfma32(ld16(dOTs + off), pb[s2], w.dvt[cb]);
-      w.dkt[cb] = mfma32(ld16(QTs + off), db[s2], w.dkt[cb]);
+      pb[i][s2] = h[64 * s2];
+      db[i][s2] = h[128 + 64 * s2];
+    }
+  }
+  // all reads in flight before the first MFMA
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < C::CB; ++i)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      dvt[i] = mfma32(ao[s2], __builtin_bit_cast(bf16x8, pb[i][s2]), dvt[i]);
+      dkt[i] = mfma32(aq[s2], __builtin_bit_cast(bf16x8, db[i][s2]), dkt[i]);
     }
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using C = KvCfg<D>;
-  __shared__ __attribute__((aligned(1024))) __bf16 stg0[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) __bf16 stg1[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) __bf16 stg2[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) __bf16 stg3[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 stages[C::NSTAGE * C::STAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 hands[2 * C::HAND];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
@@ -293,76 +353,108 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int kb = item % nkb;  // lowest key block (most causal work) first within a head
   const int bh = item / nkb;
   const int k0 = kb * C::BK;
-  const int kw = k0 + 32 * wave;
+  const int grp = wave & 3;
+  const int kw = k0 + 32 * grp;
   const int key = kw + lr;
-
-  KvWave w;
-  {
-    const __bf16* Kh = a.k + (size_t)bh * a.Tk * D;
-    const __bf16* Vh = a.v + (size_t)bh * a.Tk * D;
-    const int kr = min(key, a.Tk - 1);
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      w.kf[ks] = ld16(Kh + (size_t)kr * D + 16 * ks + 8 * hf);
-      w.vf[ks] = ld16(Vh + (size_t)kr * D + 16 * ks + 8 * hf);
-    }
-#pragma unroll
-    for (int cb = 0; cb < C::CB; ++cb) {
-      w.dkt[cb] = f32x16{};
-      w.dvt[cb] = f32x16{};
-    }
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      settle(w.kf[ks]);
-      settle(w.vf[ks]);
-    }
-  }
 
   const int nqt = (a.Tq + 31) / 32;
   const int t_begin = CAUSAL ? min(k0 / 32, nqt) : 0;
   const int n = nqt - t_begin;
-  const bool wave_active = kw < a.Tk;
+  // Query tiles are walked from the last one down, so that the key blocks of
+  // one head (neighbours on one XCD) stream the same tiles at about the same
+  // time and share them in L2.
+  auto tile = [&](int j) { return nqt - 1 - j; };
+  const bool grp_active = kw < a.Tk;
+  // a tile is skipped when every query of it precedes every key of the group
+  auto active = [&](int j) { return grp_active && !(CAUSAL && 32 * tile(j) + 31 < kw); };
+  auto stage = [&](int j) { return stages + (j % C::NSTAGE) * C::STAGE; };
+  auto hand = [&](int j) { return hands + (j & 1) * C::HAND + grp * C::HAND_GRP; };
 
-  // tiles 0..2 in flight before the loop; tile j+3 is issued at step j
-  if (n > 0) dkdv_issue<D>(a, bh, t_begin, stg0, wave, lane);
-  if (n > 1) dkdv_issue<D>(a, bh, t_begin + 1, stg1, wave, lane);
-  if (n > 2) dkdv_issue<D>(a, bh, t_begin + 2, stg2, wave, lane);
-
-  auto step = [&](int j, const __bf16* cur, __bf16* ahead) {
-    // tile j has landed once at most the copies of tiles j+1, j+2 are pending
-    const int after = min(2, n - 1 - j);
-    if (after >= 2) wait_vm<2 * C::VM>();
-    else if (after == 1) wait_vm<C::VM>();
+  // Step j (j = 0..n): tile j has landed and is published by the barrier; the
+  // copy of tile j+AHEAD goes into the stage of tile j-2; score waves work on
+  // tile j, gradient waves on tile j-1.
+  for (int j = 0; j < C::AHEAD && j < n; ++j) dkdv_issue<D>(a, bh, tile(j), stage(j), wave, lane);
+  // this wave's copies of tiles j+1 .. j+AHEAD-1 may still be in flight
+  auto wait_tile = [&](int j) {
+    const int later = min(C::AHEAD - 1, n - 1 - j);
+    if (later >= 3) wait_vm<3 * C::VM>();
+    else if (later == 2) wait_vm<2 * C::VM>();
+    else if (later == 1) wait_vm<C::VM>();
     else wait_vm<0>();
-    barrier();
-    if (j + 3 < n) dkdv_issue<D>(a, bh, t_begin + j + 3, ahead, wave, lane);
-    const int t = t_begin + j;
-    // skipped when every query of the tile precedes every key of the wave
-    if (wave_active && !(CAUSAL && 32 * t + 31 < kw)) dkdv_compute<D, CAUSAL>(a, w, cur, t, kw, lane);
   };
-  for (int j = 0; j < n; j += 4) {
-    step(j, stg0, stg3);
-    if (j + 1 < n) step(j + 1, stg1, stg0);
-    if (j + 2 < n) step(j + 2, stg2, stg1);
-    if (j + 3 < n) step(j + 3, stg3, stg2);
-  }
-
-  // dK = scale * (dK^T)^T, dV: register r of block cb is column 32cb + 8(r/4) + 4hf + r%4
-  if (key < a.Tk) {
-    __bf16* dkr = a.dk + ((size_t)bh * a.Tk + key) * D;
-    __bf16* dvr = a.dv + ((size_t)bh * a.Tk + key) * D;
+  static_assert(C::AHEAD == 4, "wait_tile covers up to 3 later tiles");
+  if (wave < 4) {
+    bf16x8 kf[8], vf[8];
+    {
+      const __bf16* Kh = a.k + (size_t)bh * a.Tk * D;
+      const __bf16* Vh = a.v + (size_t)bh * a.Tk * D;
+      const int kr = min(key, a.Tk - 1);
 #pragma unroll
-    for (int cb = 0; cb < C::CB; ++cb)
+      for (int ks = 0; ks < C::KS; ++ks) {
+        kf[ks] = ld16(Kh + (size_t)kr * D + 16 * ks + 8 * hf);
+        vf[ks] = ld16(Vh + (size_t)kr * D + 16 * ks + 8 * hf);
+      }
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        settle(kf[ks]);
+        settle(vf[ks]);
+      }
+    }
+    for (int j = 0; j <= n; ++j) {
+      wait_tile(j);
+      barrier();
+      if (j + C::AHEAD < n) dkdv_issue<D>(a, bh, tile(j + C::AHEAD), stage(j + C::AHEAD), wave, lane);
+      if (j < n) {
+        const int t = tile(j);
+        if (!active(j)) {
+          u32x4* h = reinterpret_cast<u32x4*>(hand(j)) + lane;
+          const u32x4 z = {0u, 0u, 0u, 0u};
+          h[0] = z;
+          h[64] = z;
+          h[128] = z;
+          h[192] = z;
+        } else if (CAUSAL && 32 * t < kw + 31) {
+          dkdv_scores<D, true>(a, kf, vf, stage(j), hand(j), t, kw, lane);
+        } else {
+          dkdv_scores<D, false>(a, kf, vf, stage(j), hand(j), t, kw, lane);
+        }
+      }
+    }
+  } else {
+    f32x16 dkt[4], dvt[4];
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb) {
+      dkt[cb] = f32x16{};
+      dvt[cb] = f32x16{};
+    }
+    for (int j = 0; j <= n; ++j) {
+      wait_tile(j);
+      barrier();
+      if (j + C::AHEAD < n) dkdv_issue<D>(a, bh, tile(j + C::AHEAD), stage(j + C::AHEAD), wave, lane);
+      // every tile in range has an active key group (the first one); score
+      // waves of inactive groups hand over zeros
+      if (j >= 1) dkdv_grads<D>(dkt, dvt, stage(j - 1), hands + ((j - 1) & 1) * C::HAND, grp, lane);
+    }
+    // dK = scale * (dK^T)^T, dV: register r of accumulator i is column
+    // 32cb + 8(r/4) + 4hf + r%4 of key k0 + 32 kgroup(grp, i) + lane%32
+    const int cb = grp % C::CB;
+#pragma unroll
+    for (int i = 0; i < C::CB; ++i) {
+      const int kk = k0 + 32 * C::kgroup(grp, i) + lr;
+      if (kk >= a.Tk) continue;
+      __bf16* dkr = a.dk + ((size_t)bh * a.Tk + kk) * D;
+      __bf16* dvr = a.dv + ((size_t)bh * a.Tk + kk) * D;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int c = 32 * cb + 8 * g + 4 * hf;
-        const u32x2 wk = {pack_bf16x2(w.dkt[cb][4 * g] * a.scale, w.dkt[cb][4 * g + 1] * a.scale),
-                          pack_bf16x2(w.dkt[cb][4 * g + 2] * a.scale, w.dkt[cb][4 * g + 3] * a.scale)};
-        const u32x2 wv = {pack_bf16x2(w.dvt[cb][4 * g], w.dvt[cb][4 * g + 1]),
-                          pack_bf16x2(w.dvt[cb][4 * g + 2], w.dvt[cb][4 * g + 3])};
+        const u32x2 wk = {pack_bf16x2(dkt[i][4 * g] * a.scale, dkt[i][4 * g + 1] * a.scale),
+                          pack_bf16x2(dkt[i][4 * g + 2] * a.scale, dkt[i][4 * g + 3] * a.scale)};
+        const u32x2 wv = {pack_bf16x2(dvt[i][4 * g], dvt[i][4 * g + 1]),
+                          pack_bf16x2(dvt[i][4 * g + 2], dvt[i][4 * g + 3])};
         *reinterpret_cast<u32x2*>(dkr + c) = wk;
         *reinterpret_cast<u32x2*>(dvr + c) = wv;
       }
+    }
   }
 }
 
@@ -534,18 +626,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------------
 struct BwdLayout {
-  size_t stats, qt, dot, kt, total;
+  size_t stats, kt, total;
 };
 
 BwdLayout bwd_layout(int BH, int Tq, int Tk, int d) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   const size_t nqb32 = (size_t)(Tq + 31) / 32;
-  const size_t tq_pad = (size_t)(Tq + 63) / 64 * 64, tk_pad = (size_t)(Tk + 63) / 64 * 64;
+  const size_t tk_pad = (size_t)(Tk + 63) / 64 * 64;
   BwdLayout L;
   L.stats = 0;
-  L.qt = up(L.stats + (size_t)BH * nqb32 * 64 * sizeof(float));
-  L.dot = up(L.qt + (size_t)BH * d * tq_pad * 2);
-  L.kt = up(L.dot + (size_t)BH * d * tq_pad * 2);
+  L.kt = up(L.stats + (size_t)BH * nqb32 * 64 * sizeof(float));
   L.total = up(L.kt + (size_t)BH * d * tk_pad * 2);
   return L;
 }
@@ -553,25 +643,14 @@ BwdLayout bwd_layout(int BH, int Tq, int Tk, int d) {
 template <int D>
 hipError_t bwd_launch_d(BwdArgs& args, const __bf16* o, const float* lse, bool causal, char* ws,
                         const BwdLayout& L, hipStream_t stream) {
-  // pre-pass: row statistics and transposed copies
+  // pre-pass: row statistics and the transposed copy of K
   prof_begin(2, stream);
   {
     const int rows = args.BH * args.nqb32 * 32;
     hipLaunchKernelGGL(bwd_stats_kernel<D>, dim3((rows * 16 + 255) / 256), dim3(256), 0, stream, o, args.dout, lse,
                        reinterpret_cast<float*>(ws + L.stats), args.BH, args.Tq, args.nqb32);
-    TransposeArgs t;
-    t.in[0] = args.q;
-    t.in[1] = args.dout;
-    t.in[2] = args.k;
-    t.out[0] = reinterpret_cast<__bf16*>(ws + L.qt);
-    t.out[1] = reinterpret_cast<__bf16*>(ws + L.dot);
-    t.out[2] = reinterpret_cast<__bf16*>(ws + L.kt);
-    t.T[0] = t.T[1] = args.Tq;
-    t.T[2] = args.Tk;
-    t.Tpad[0] = t.Tpad[1] = args.Tq_pad;
-    t.Tpad[2] = args.Tk_pad;
-    const int blocks = max(args.Tq_pad, args.Tk_pad) / 64;
-    hipLaunchKernelGGL(bwd_transpose_kernel<D>, dim3(blocks, args.BH, 3), dim3(256), 0, stream, t);
+    hipLaunchKernelGGL(bwd_transpose_kernel<D>, dim3(args.Tk_pad / 64, args.BH), dim3(256), 0, stream, args.k,
+                       reinterpret_cast<__bf16*>(ws + L.kt), args.Tk, args.Tk_pad);
   }
   prof_end(2, stream);
   hipError_t e = hipGetLastError();
@@ -580,9 +659,9 @@ hipError_t bwd_launch_d(BwdArgs& args, const __bf16* o, const float* lse, bool c
   const int nkb = (args.Tk + KvCfg<D>::BK - 1) / KvCfg<D>::BK;
   prof_begin(3, stream);
   if (causal)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(args.BH * nkb), dim3(256), 0, stream, args);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(args.BH * nkb), dim3(512), 0, stream, args);
   else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(args.BH * nkb), dim3(256), 0, stream, args);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(args.BH * nkb), dim3(512), 0, stream, args);
   prof_end(3, stream);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -612,8 +691,6 @@ hipError_t bwd_bf16_launch(const void* q, const void* k, const void* v, const vo
   a.v = static_cast<const __bf16*>(v);
   a.dout = static_cast<const __bf16*>(dout);
   a.stats = reinterpret_cast<const float*>(ws + L.stats);
-  a.qt = reinterpret_cast<const __bf16*>(ws + L.qt);
-  a.dot = reinterpret_cast<const __bf16*>(ws + L.dot);
   a.kt = reinterpret_cast<const __bf16*>(ws + L.kt);
   a.dq = static_cast<__bf16*>(dq);
   a.dk = static_cast<__bf16*>(dk);
@@ -621,7 +698,6 @@ hipError_t bwd_bf16_launch(const void* q, const void* k, const void* v, const vo
   a.BH = BH;
   a.Tq = Tq;
   a.Tk = Tk;
-  a.Tq_pad = (Tq + 63) / 64 * 64;
   a.Tk_pad = (Tk + 63) / 64 * 64;
   a.nqb32 = (Tq + 31) / 32;
   a.scale = scale;

@@ -110,8 +110,9 @@ int attn_fwd_splits(const void* q, const void* k, const void* v, void* o, float*
  * dK, dV come from one kernel that walks the queries of each key block and
  * dQ from another that walks the keys of each query block, so every output
  * element is summed in a fixed order by one workgroup: results are
- * deterministic.  Workspace (row statistics and transposed copies of Q, dO,
- * K: about 3 * B*H*T*d*2 bytes) is allocated with hipMallocAsync on `stream`.
+ * deterministic.  Workspace (row statistics and a transposed copy of K:
+ * about B*H*(Tq*8 + Tk*d*2) bytes) is allocated with hipMallocAsync on
+ * `stream`.
  * Supported: d == dv, d in {64, 128}; otherwise ATTN_ERR_UNSUPPORTED.
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -156,7 +157,7 @@ int attn_bwd_f32(const float* q, const float* k, const float* v, const float* o,
  */
 #define ATTN_KERNEL_FWD 0            /* forward main kernel */
 #define ATTN_KERNEL_FWD_COMBINE 1    /* merge of key-split partial states */
-#define ATTN_KERNEL_BWD_PREP 2       /* D = rowsum(dO o O), LSE*log2(e), transposed Q, dO, K */
+#define ATTN_KERNEL_BWD_PREP 2       /* D = rowsum(dO o O), LSE*log2(e), transposed K */
 #define ATTN_KERNEL_BWD_DKDV 3       /* backward: dK and dV */
 #define ATTN_KERNEL_BWD_DQ 4         /* backward: dQ */
 #define ATTN_KERNEL_KINDS 5
