@@ -203,7 +203,7 @@ def main(argv=None) -> int:
     pairs, fwd_fl, bwd_fl, fwd_b, bwd_b = work(w)
     ms_step = (t1 - t0) * 1e3 / args.steps
     total_tflops = (fwd_fl + bwd_fl) / (ms_step * 1e-3) / 1e12
-    fwd_ms = (kern["fwd"][0] + kern["fwd_combine"][0]) / args.steps
+    fwd_ms = (kern["fwd"][0] + kern["fwd_aux"][0]) / args.steps
     bwd_ms = (kern["bwd_prep"][0] + kern["bwd_dkdv"][0] + kern["bwd_dq"][0]) / args.steps
     fwd_tflops = fwd_fl / (fwd_ms * 1e-3) / 1e12 if fwd_ms > 0 else None
     bwd_tflops = bwd_fl / (bwd_ms * 1e-3) / 1e12 if bwd_ms > 0 else None

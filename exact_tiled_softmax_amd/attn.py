@@ -26,11 +26,11 @@ EXPORTED = ("attn_fwd", "attn_fwd_splits", "attn_bwd", "attn_fwd_f32", "attn_bwd
 
 # kernel kinds of attn_profile_query (include/attn.h)
 KERNEL_FWD = 0
-KERNEL_FWD_COMBINE = 1
+KERNEL_FWD_AUX = 1
 KERNEL_BWD_PREP = 2
 KERNEL_BWD_DKDV = 3
 KERNEL_BWD_DQ = 4
-KERNEL_NAMES = {0: "fwd", 1: "fwd_combine", 2: "bwd_prep", 3: "bwd_dkdv", 4: "bwd_dq"}
+KERNEL_NAMES = {0: "fwd", 1: "fwd_aux", 2: "bwd_prep", 3: "bwd_dkdv", 4: "bwd_dq"}
 
 _lib = None
 

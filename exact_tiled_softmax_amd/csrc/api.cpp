@@ -54,7 +54,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int BH = B * H;
   const int splits = attn::fwd_bf16_num_splits(BH, Tq, Tk, causal, num_splits);
-  const size_t ws_bytes = attn::fwd_bf16_workspace_bytes(BH, Tq, d, splits);
+  const size_t ws_bytes = attn::fwd_bf16_workspace_bytes(BH, Tq, Tk, d, splits);
   void* ws = nullptr;
   if (ws_bytes) {
     hipError_t e = hipMallocAsync(&ws, ws_bytes, s);

@@ -17,7 +17,7 @@ void prof_end(int kind, hipStream_t stream);
 // Number of key splits to use (requested <= 0: heuristic), clamped to the number
 // of 64-key blocks.
 int fwd_bf16_num_splits(int BH, int Tq, int Tk, int causal, int requested);
-size_t fwd_bf16_workspace_bytes(int BH, int Tq, int d, int num_splits);
+size_t fwd_bf16_workspace_bytes(int BH, int Tq, int Tk, int d, int num_splits);
 hipError_t fwd_bf16_launch(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Tq,
                            int Tk, int d, float scale, int causal, int num_splits, void* workspace,
                            hipStream_t stream);

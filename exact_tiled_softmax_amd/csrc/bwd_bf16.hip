@@ -35,66 +35,11 @@
 // tiles ahead of the compute.
 #include "attn_common.hpp"
 #include "attn_launch.hpp"
+#include "tile_stream.hpp"
 
 namespace attn {
 
 namespace {
-
-typedef __attribute__((address_space(3))) const void lds_cvoid;
-
-// One wave copies 16 bytes per lane from `src` (per lane) to LDS; lane l's
-// bytes land at lds_base + 16*l (lds_base must be the same in every lane).
-// Issued as inline assembly so that the compiler neither reorders LDS
-// accesses across it nor adds waits of its own for it: every copy is waited
-// for explicitly (wait_vm) before a barrier that publishes the tile.
-__device__ __forceinline__ void dma16(const __bf16* src, const __bf16* lds_base) {
-  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_cvoid*)lds_base));
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
-}
-
-// Wait until at most N vector-memory operations of this wave are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-
-// Workgroup barrier after this wave's LDS reads and writes have completed;
-// it also keeps the compiler from moving memory accesses across it.  Tile
-// copies into LDS are waited for separately (wait_vm) before it.
-__device__ __forceinline__ void barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-__device__ __forceinline__ bf16x8 ld16(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
-
-// Make the compiler complete a register load here, before the tile copies
-// that follow are issued: its own waits count only its own loads, so a wait
-// for this value inside the tile loop would also drain the copies.
-__device__ __forceinline__ void settle(const bf16x8& x) { asm volatile("" ::"v"(__builtin_bit_cast(u32x4, x))); }
-__device__ __forceinline__ void settle(float x) { asm volatile("" ::"v"(x)); }
-
-// Swizzle of a row-major LDS tile with CPR 16-byte chunks per row: logical
-// chunk c of row r is stored at chunk r*CPR + (c ^ swz<CPR>(r)).  For every
-// CPR, 16 consecutive rows read at one logical chunk hit 16 different
-// 16-byte bank groups (a 16-byte read of 32 rows has no bank conflict), and
-// for CPR 8 and 16 the 4 rows x 4 chunks that half a wave touches in a
-// transposing read (rows 4a..4a+3, chunks 4m..4m+3) are 16 different bank
-// groups as well.
-template <int CPR>
-__device__ __forceinline__ int swz(int r) {
-  static_assert(CPR == 4 || CPR == 8 || CPR == 16, "chunks per row");
-  if constexpr (CPR == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
-  else if constexpr (CPR == 8) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-  else return (r >> 2) & 3;
-}
-
-// Row of a 16-row group that the transposed copies store at position p
-// (0..15).  An MFMA accumulator gives lane half h the rows 4h..4h+3 and
-// 8+4h..8+4h+3 of each 16-row group, and an operand read takes 8 consecutive
-// positions, so position 8h+e holds row (e < 4 ? 4h+e : 8+4h+e-4).
-__device__ __forceinline__ int group_row(int p) {
-  const int h = (p >> 3) & 1, e = p & 7;
-  return (e < 4) ? 4 * h + e : 8 + 4 * h + (e - 4);
-}
 
 struct BwdArgs {
   const __bf16* q;
@@ -142,41 +87,6 @@ __global__ __launch_bounds__(256) void bwd_stats_kernel(const __bf16* __restrict
     float* blk = stats + ((size_t)bh * nqb32 + qi / 32) * 64;
     blk[qi % 32] = l2;
     blk[32 + qi % 32] = ok ? acc : 0.f;
-  }
-}
-
-// bwd_transpose: one 64-row block of one head per workgroup.
-// out[bh][c][tpos] = in[bh][t][c] with t = 16*(tpos/16) + group_row(tpos%16),
-// zero for t >= T.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_transpose_kernel(const __bf16* __restrict__ in_all,
-                                                            __bf16* __restrict__ out_all, int T, int Tpad) {
-  constexpr int STR = D + 8;
-  constexpr int CPR = D / 8;
-  __shared__ __attribute__((aligned(16))) __bf16 tile[64 * STR];
-  const int bh = blockIdx.y;
-  const int t0 = blockIdx.x * 64;
-  const __bf16* in = in_all + (size_t)bh * T * D;
-  __bf16* out = out_all + (size_t)bh * D * Tpad;
-  for (int c = threadIdx.x; c < 64 * CPR; c += 256) {
-    const int r = c / CPR, col = (c % CPR) * 8;
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (t0 + r < T) x = *reinterpret_cast<const u32x4*>(in + (size_t)(t0 + r) * D + col);
-    *reinterpret_cast<u32x4*>(tile + r * STR + col) = x;
-  }
-  __syncthreads();
-  const uint16_t* ts = reinterpret_cast<const uint16_t*>(tile);
-  for (int it = threadIdx.x; it < D * 8; it += 256) {
-    const int c = it / 8, m = it % 8;  // output row c, positions 8m..8m+7
-    unsigned w[4];
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const int p0 = 8 * m + e, p1 = p0 + 1;
-      const int r0 = (p0 & ~15) + group_row(p0 & 15), r1 = (p1 & ~15) + group_row(p1 & 15);
-      w[e / 2] = (unsigned)ts[r0 * STR + c] | ((unsigned)ts[r1 * STR + c] << 16);
-    }
-    const u32x4 v = {w[0], w[1], w[2], w[3]};
-    *reinterpret_cast<u32x4*>(out + (size_t)c * Tpad + t0 + 8 * m) = v;
   }
 }
 
@@ -499,6 +409,23 @@ __device__ __forceinline__ void dq_issue(const BwdArgs& a, int bh, int j, __bf16
   }
 }
 
+// dS^T of one 32-key unit as bf16 B operands: accumulator register r is key
+// key0 + 8(r/4) + 4hf + r%4 for query my_q.  MASK: the unit holds a blocked
+// (key, query) pair (causal diagonal or keys past Tk).
+template <bool CAUSAL, bool MASK>
+__device__ __forceinline__ void dq_softmax(const BwdArgs& a, const DqWave& w, const f32x16& st, const f32x16& dpt,
+                                           int key0, int my_q, int hf, bf16x8 (&db)[2]) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float p = fast_exp2(__builtin_fmaf(st[r], a.scale_log2, -w.lse2));
+    if (MASK) {
+      const int kk = key0 + 8 * (r / 4) + 4 * hf + (r % 4);
+      p = ((CAUSAL && kk > my_q) || kk >= a.Tk) ? 0.f : p;
+    }
+    db[r / 8][r % 8] = to_bf16(p * (dpt[r] - w.dsum));
+  }
+}
+
 template <int D, bool CAUSAL>
 __device__ __forceinline__ void dq_compute(const BwdArgs& a, DqWave& w, const __bf16* stg, int j, int qw, int kend,
                                            int lane) {
@@ -514,25 +441,17 @@ __device__ __forceinline__ void dq_compute(const BwdArgs& a, DqWave& w, const __
   for (int u = 0; u < 2; ++u) {
     const int key0 = 64 * j + 32 * u;
     if (key0 >= kend) break;
+    // the S^T and dP^T chains alternate
     f32x16 st = {}, dpt = {};
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-      st = mfma32(ld16(Ks + (32 * u + lr) * D + 8 * ((2 * ks + hf) ^ rsw)), w.qf[ks], st);
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-      dpt = mfma32(ld16(Vs + (32 * u + lr) * D + 8 * ((2 * ks + hf) ^ rsw)), w.df[ks], dpt);
-    // accumulator register r: key key0 + 8(r/4) + 4hf + r%4, query my_q
-    const bool need_mask = (CAUSAL && key0 + 31 > qw) || key0 + 32 > a.Tk;
-    bf16x8 db[2];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float p = fast_exp2(__builtin_fmaf(st[r], a.scale_log2, -w.lse2));
-      if (need_mask) {
-        const int kk = key0 + 8 * (r / 4) + 4 * hf + (r % 4);
-        p = ((CAUSAL && kk > my_q) || kk >= a.Tk) ? 0.f : p;
-      }
-      db[r / 8][r % 8] = to_bf16(p * (dpt[r] - w.dsum));
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const int off = (32 * u + lr) * D + 8 * ((2 * ks + hf) ^ rsw);
+      st = mfma32(ld16(Ks + off), w.qf[ks], st);
+      dpt = mfma32(ld16(Vs + off), w.df[ks], dpt);
     }
+    bf16x8 db[2];
+    if ((CAUSAL && key0 + 31 > qw) || key0 + 32 > a.Tk) dq_softmax<CAUSAL, true>(a, w, st, dpt, key0, my_q, hf, db);
+    else dq_softmax<CAUSAL, false>(a, w, st, dpt, key0, my_q, hf, db);
 #pragma unroll
     for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
@@ -649,7 +568,7 @@ hipError_t bwd_launch_d(BwdArgs& args, const __bf16* o, const float* lse, bool c
     const int rows = args.BH * args.nqb32 * 32;
     hipLaunchKernelGGL(bwd_stats_kernel<D>, dim3((rows * 16 + 255) / 256), dim3(256), 0, stream, o, args.dout, lse,
                        reinterpret_cast<float*>(ws + L.stats), args.BH, args.Tq, args.nqb32);
-    hipLaunchKernelGGL(bwd_transpose_kernel<D>, dim3(args.Tk_pad / 64, args.BH), dim3(256), 0, stream, args.k,
+    hipLaunchKernelGGL(transpose_rows_kernel<D>, dim3(args.Tk_pad / 64, args.BH), dim3(256), 0, stream, args.k,
                        reinterpret_cast<__bf16*>(ws + L.kt), args.Tk, args.Tk_pad);
   }
   prof_end(2, stream);

@@ -6,21 +6,24 @@
 // Attention", section "Chunk-wise Mode with Online Softmax Re-scale": query
 // tiles outside, key tiles inside).  Each wave owns 32 rows and keeps, per
 // row, the running max m, running sum l and accumulator a of "Tiled attention
-// with an online softmax", section "Task", in registers.  K/V are streamed in
-// tiles of 64 keys through double-buffered LDS; each tile is consumed as two
-// 32-key online-softmax steps.
+// with an online softmax", section "Task", in registers; its Q rows stay in
+// registers as MFMA operands.  K and V^T are streamed in tiles of 64 keys
+// through a 4-stage LDS ring filled by direct-to-LDS copies, three tiles
+// ahead of the compute (V^T is a transposed copy of V made first, in the
+// workspace).
 //
-// Per 32-key step and wave:
+// Per 64-key tile and wave:
 //   S^T = K Q^T           32x32x16 bf16 MFMA, fp32 accumulators, keys on the
 //                         M side so that every lane holds one query row's
-//                         scores in registers (a row reduction is 16 registers
+//                         scores in registers (a row reduction is 32 registers
 //                         plus one exchange between the lane halves)
 //   mask                  causal (key > query) and ragged tails -> blocked
+//                         (diagonal and tail tiles only)
 //   m  = max(m, rowmax)   scores in log2 units (multiplied by scale*log2(e))
 //   P  = exp2(s - m), l += rowsum(P), a += V^T P^T  (P rounded to bf16)
 // Epilogue: O = a / l, LSE = (m + log2 l) * ln 2.
 //
-// The reference max m used in the exponent is only moved when a row's block
+// The reference max m used in the exponent is only moved when a row's tile
 // max exceeds it by more than kTau (log2 units); then l and a are rescaled by
 // exp2(m_old - m_new) as in the page's recurrence.  Between moves P <= 2^kTau,
 // and O = a / l and LSE = m + log2 l are the same quantities for any m (the
@@ -28,173 +31,114 @@
 // rescale of a off the common path.  A row with no allowed key yet keeps
 // m = -inf and uses 0 in its exponent (the page's guard).
 //
-// LDS layout per stage: K row-major [64][D+8] (MFMA A operand rows, 16-byte
-// reads); V transposed, V^T[c][64 keys] with rows of 80 elements, the 4-key
-// groups of each 16-key MFMA step ordered so that the 8 keys one lane feeds
-// into an MFMA are contiguous, and the 16-byte units XOR-swizzled by (c >> 3)
-// (conflict-free 16-byte reads and at most 2-way conflicts on the 8-byte
-// transposing writes).
-//
 // With key splits, each workgroup covers one contiguous key range and stores
 // its unnormalised state (m, l, a) in fp32; a second kernel merges the states
 // of a row with the same rescale rule and writes O and LSE.
 #include "attn_common.hpp"
 #include "attn_launch.hpp"
+#include "tile_stream.hpp"
 
 namespace attn {
 
 namespace {
 
-constexpr int kFwdWaves = 8;
-constexpr int kFwdThreads = kFwdWaves * 64;
-constexpr int kBM = 32 * kFwdWaves;  // query rows per workgroup
-constexpr int kBN = 64;              // keys per K/V tile
-constexpr int kVtStr = 80;           // V^T row stride (elements)
-constexpr float kTau = 8.f;          // lazy-rescale threshold (log2 units)
+constexpr float kTau = 8.f;  // lazy-rescale threshold (log2 units)
 
 template <int D>
 struct FwdCfg {
-  static constexpr int KS = D / 16;                  // MFMA k-steps over the head dim
-  static constexpr int CB = D / 32;                  // 32-wide blocks of the value dim
-  static constexpr int KSTR = D + 8;                 // K row stride (elements)
-  static constexpr int KTILE = kBN * KSTR;           // elements of a K stage
-  static constexpr int VTILE = D * kVtStr;           // elements of a V^T stage
-  static constexpr int STAGE = KTILE + VTILE;
-  static constexpr int KCHUNKS = kBN * D / 8;        // 16-byte chunks of a K tile
-  static constexpr int KPER = KCHUNKS / kFwdThreads;
-  static constexpr int VTASKS = kBN * D / 16;        // 4 keys x 4 columns per task
-  static_assert(KCHUNKS % kFwdThreads == 0, "K tile must split evenly over threads");
-  static_assert(VTASKS <= kFwdThreads, "one V task per thread at most");
+  static constexpr int KS = D / 16;                      // MFMA k-steps over the head dim
+  static constexpr int CB = D / 32;                      // 32-wide blocks of the value dim
+  static constexpr int CPR = D / 8;                      // 16-byte chunks per K row
+  static constexpr int WAVES = 8;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int BM = 32 * WAVES;                  // query rows per workgroup
+  static constexpr int BN = 64;                          // keys per tile
+  static constexpr int TILE = BN * D;                    // bf16 elements of a K tile and of a V^T tile
+  static constexpr int PER_TENSOR = TILE * 2 / 1024;     // wave copies per tensor and tile
+  static constexpr int PER_WAVE = 2 * PER_TENSOR / WAVES;
+  static constexpr int VM = PER_WAVE;                    // vector-memory ops per wave and tile
+  static constexpr int STAGE = 2 * TILE;
+  static constexpr int NSTAGE = 4;
+  static constexpr int AHEAD = NSTAGE - 1;               // tiles in flight ahead of the compute
+  static_assert(PER_WAVE >= 1 && 2 * PER_TENSOR == PER_WAVE * WAVES, "tile copy split");
 };
-
-// position of 4-key group G (0..15) inside a V^T row: swap bits 0 and 1, so
-// groups (8b+4u+h) and (8b+4u+2+h) become adjacent (one lane's 8 keys)
-__device__ __forceinline__ int vt_group_pos(int g) { return (g & ~3) | ((g & 1) << 1) | ((g >> 1) & 1); }
-
-// element offset of (column c, 16-byte unit U) in a V^T stage
-__device__ __forceinline__ int vt_off(int c, int unit) { return c * kVtStr + ((unit ^ ((c >> 3) & 7)) << 3); }
-
-template <int D>
-struct TileRegs {
-  u32x4 k[FwdCfg<D>::KPER];
-  u32x2 v[4];
-};
-
-// Global -> registers for one K/V tile (keys >= key_lim read as zero).
-template <int D>
-__device__ __forceinline__ void load_tile(const __bf16* __restrict__ Kh, const __bf16* __restrict__ Vh, int key0,
-                                          int key_lim, int tid, TileRegs<D>& r) {
-  using C = FwdCfg<D>;
-  constexpr int CPR = D / 8;
-#pragma unroll
-  for (int i = 0; i < C::KPER; ++i) {
-    const int c = tid + i * kFwdThreads;
-    const int row = c / CPR, col = (c % CPR) * 8;
-    const int key = key0 + row;
-    r.k[i] = key < key_lim ? *reinterpret_cast<const u32x4*>(Kh + (size_t)key * D + col) : u32x4{0u, 0u, 0u, 0u};
-  }
-  if (tid < C::VTASKS) {
-    constexpr int CG = D / 4;  // column groups
-    const int kg = tid / CG, cg = tid % CG;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = key0 + 4 * kg + j;
-      r.v[j] = key < key_lim ? *reinterpret_cast<const u32x2*>(Vh + (size_t)key * D + 4 * cg) : u32x2{0u, 0u};
-    }
-  }
-}
-
-// Registers -> LDS stage: K rows as is, V transposed into V^T.
-template <int D>
-__device__ __forceinline__ void store_tile(__bf16* stage, int tid, const TileRegs<D>& r) {
-  using C = FwdCfg<D>;
-  constexpr int CPR = D / 8;
-#pragma unroll
-  for (int i = 0; i < C::KPER; ++i) {
-    const int c = tid + i * kFwdThreads;
-    const int row = c / CPR, col = (c % CPR) * 8;
-    *reinterpret_cast<u32x4*>(stage + row * C::KSTR + col) = r.k[i];
-  }
-  if (tid < C::VTASKS) {
-    constexpr int CG = D / 4;
-    const int kg = tid / CG, cg = tid % CG;
-    const int pos = vt_group_pos(kg);
-    __bf16* vt = stage + C::KTILE;
-    // r.v[j] = {c0 c1 | c2 c3} of key 4kg+j; write {k0 k1 | k2 k3} of each column
-    const u32x2 w0 = {pack_lo16(r.v[0][0], r.v[1][0]), pack_lo16(r.v[2][0], r.v[3][0])};
-    const u32x2 w1 = {pack_hi16(r.v[0][0], r.v[1][0]), pack_hi16(r.v[2][0], r.v[3][0])};
-    const u32x2 w2 = {pack_lo16(r.v[0][1], r.v[1][1]), pack_lo16(r.v[2][1], r.v[3][1])};
-    const u32x2 w3 = {pack_hi16(r.v[0][1], r.v[1][1]), pack_hi16(r.v[2][1], r.v[3][1])};
-    const int c0 = 4 * cg, unit = pos >> 1, half = (pos & 1) * 4;
-    *reinterpret_cast<u32x2*>(vt + vt_off(c0 + 0, unit) + half) = w0;
-    *reinterpret_cast<u32x2*>(vt + vt_off(c0 + 1, unit) + half) = w1;
-    *reinterpret_cast<u32x2*>(vt + vt_off(c0 + 2, unit) + half) = w2;
-    *reinterpret_cast<u32x2*>(vt + vt_off(c0 + 3, unit) + half) = w3;
-  }
-}
 
 struct FwdArgs {
   const __bf16* q;
   const __bf16* k;
-  const __bf16* v;
+  const __bf16* vt;  // V^T [BH][D][Tk_pad], keys of each 16-key group in group_row order
   __bf16* o;
   float* lse;
   float* part_acc;  // [splits][BH][Tq][D]   (split mode)
   float* part_ml;   // [splits][BH][Tq][2]   (split mode: m in log2 units, l)
-  int BH, Tq, Tk;
+  int BH, Tq, Tk, Tk_pad;
   int num_qtiles, num_splits, keys_per_split;
   float scale_log2;  // scale * log2(e)
 };
 
+// Copies of one K tile and one V^T tile (keys key0 .. key0+63) into a stage.
+template <int D>
+__device__ __forceinline__ void fwd_issue(const FwdArgs& a, int bh, int key0, __bf16* stg, int wave, int lane) {
+  using C = FwdCfg<D>;
+  const __bf16* Kh = a.k + (size_t)bh * a.Tk * D;
+  const __bf16* VTh = a.vt + (size_t)bh * D * a.Tk_pad;
+#pragma unroll
+  for (int n = 0; n < C::PER_WAVE; ++n) {
+    const int cpy = wave * C::PER_WAVE + n;  // wave-uniform
+    const int tensor = cpy / C::PER_TENSOR, i = cpy % C::PER_TENSOR;
+    const int p = 64 * i + lane;
+    __bf16* dst = stg + tensor * C::TILE + 512 * i;
+    if (tensor == 0) {
+      const int row = p / C::CPR, c = (p % C::CPR) ^ swz<C::CPR>(row);
+      const int kk = min(key0 + row, a.Tk - 1);
+      dma16(Kh + (size_t)kk * D + 8 * c, dst);
+    } else {
+      const int rt = p / 8, ct = (p % 8) ^ swz<8>(rt);
+      dma16(VTh + (size_t)rt * a.Tk_pad + key0 + 8 * ct, dst);
+    }
+  }
+}
+
 // One 64-key tile for one wave: S^T for both 32-key blocks, row max and
-// reference-max update, then P and a += V^T P^T block by block.
+// reference-max update, then P and a += V^T P^T.
 //
 // Blocked keys (need_mask: causal diagonal or ragged tail) are handled by
 // scaling the scores in place and writing -inf for blocked ones, after which
 // the shared code runs with a unit scale: exp2(-inf - mu) = 0 exactly, also
 // when scale == 0.  A row with no allowed key yet (m_ref = -inf) uses mu = 0.
 template <int D>
-__device__ __forceinline__ void fwd_tile(const __bf16* Ks, const __bf16* Vt, const bf16x8 (&qf)[D / 16],
-                                         f32x16 (&acc)[D / 32], float& m_ref, float& l_run, float c, int lr, int hf,
-                                         bool need_mask, int key_r0, int kend, int row, bool causal) {
+__device__ __forceinline__ void fwd_tile(const __bf16* stg, const bf16x8 (&qf)[8], f32x16 (&acc)[4], float& m_ref,
+                                         float& l_run, float c, int lane, bool need_mask, int key0, int kend, int row,
+                                         bool causal) {
   using C = FwdCfg<D>;
-  f32x16 s0 = f32x16{}, s1 = f32x16{};
-  {
-    bf16x8 kf[C::KS];
+  const int lr = lane % 32, hf = lane / 32;
+  const __bf16* Ks = stg;
+  const __bf16* VTs = stg + C::TILE;
+  const int rsw = swz<C::CPR>(lr), tsw = swz<8>(lr);
+  // the two 32-key score chains alternate
+  f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-      kf[ks] = *reinterpret_cast<const bf16x8*>(Ks + lr * C::KSTR + 16 * ks + 8 * hf);
+  for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) s0 = mfma32(kf[ks], qf[ks], s0);
-  }
-  {
-    bf16x8 kf[C::KS];
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-      kf[ks] = *reinterpret_cast<const bf16x8*>(Ks + (32 + lr) * C::KSTR + 16 * ks + 8 * hf);
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) s1 = mfma32(kf[ks], qf[ks], s1);
-  }
-  bf16x8 vf[2][C::CB];
-#pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int cb = 0; cb < C::CB; ++cb) vf[u][cb] = *reinterpret_cast<const bf16x8*>(Vt + vt_off(32 * cb + lr, 2 * u + hf));
+    for (int u = 0; u < 2; ++u)
+      s[u] = mfma32(ld16(Ks + (32 * u + lr) * D + 8 * ((2 * ks + hf) ^ rsw)), qf[ks], s[u]);
 
+  // accumulator register r of block u: key key0 + 32u + 8(r/4) + 4hf + r%4
   float cc = c;
   if (need_mask) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = key_r0 + 8 * (r / 4) + (r % 4);
-      s0[r] = (key >= kend || (causal && key > row)) ? -INFINITY : s0[r] * c;
-      s1[r] = (key + 32 >= kend || (causal && key + 32 > row)) ? -INFINITY : s1[r] * c;
-    }
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 32 * u + 8 * (r / 4) + 4 * hf + (r % 4);
+        s[u][r] = (key >= kend || (causal && key > row)) ? -INFINITY : s[u][r] * c;
+      }
     cc = 1.f;
   }
   // ---- row max and reference-max update -----------------------------------------
-  float mx = fmaxf(s0[0], s1[0]);
+  float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
-  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
   mx = pair_max(mx);
   const float mt = (mx == -INFINITY) ? -INFINITY : mx * cc;
   const bool move = mt > m_ref + kTau;
@@ -209,55 +153,32 @@ __device__ __forceinline__ void fwd_tile(const __bf16* Ks, const __bf16* Vt, con
     m_ref = m_new;
   }
   const float mu = (m_ref == -INFINITY) ? 0.f : m_ref;
-  // ---- block 0: P, row sum, a += V^T P^T ------------------------------------------
+  // ---- P (bf16 B operand: k-slot 8hf+e of step s2 = register 8*s2 + e) ------------
   float psum = 0.f;
-  bf16x8 p0, p1;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float x = fast_exp2(__builtin_fmaf(s0[e], cc, -mu));
-    const float y = fast_exp2(__builtin_fmaf(s0[8 + e], cc, -mu));
-    psum += x + y;
-    p0[e] = to_bf16(x);
-    p1[e] = to_bf16(y);
-  }
-#pragma unroll
-  for (int cb = 0; cb < C::CB; ++cb) acc[cb] = mfma32(vf[0][cb], p0, acc[cb]);
-#pragma unroll
-  for (int cb = 0; cb < C::CB; ++cb) acc[cb] = mfma32(vf[1][cb], p1, acc[cb]);
-  // ---- block 1 --------------------------------------------------------------------
+  bf16x8 pb[2][2];
 #pragma unroll
   for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int cb = 0; cb < C::CB; ++cb)
-      vf[u][cb] = *reinterpret_cast<const bf16x8*>(Vt + vt_off(32 * cb + lr, 4 + 2 * u + hf));
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float x = fast_exp2(__builtin_fmaf(s1[e], cc, -mu));
-    const float y = fast_exp2(__builtin_fmaf(s1[8 + e], cc, -mu));
-    psum += x + y;
-    p0[e] = to_bf16(x);
-    p1[e] = to_bf16(y);
-  }
+    for (int r = 0; r < 16; ++r) {
+      const float x = fast_exp2(__builtin_fmaf(s[u][r], cc, -mu));
+      psum += x;
+      pb[u][r / 8][r % 8] = to_bf16(x);
+    }
   l_run += psum;
+  // ---- a += V^T P^T -----------------------------------------------------------------
 #pragma unroll
-  for (int cb = 0; cb < C::CB; ++cb) acc[cb] = mfma32(vf[0][cb], p0, acc[cb]);
+  for (int u = 0; u < 2; ++u)
 #pragma unroll
-  for (int cb = 0; cb < C::CB; ++cb) acc[cb] = mfma32(vf[1][cb], p1, acc[cb]);
-#if ATTN_FWD_SCHED
-  // interleave the second block's exponentials (VALU) with the first block's
-  // P V MFMAs
+    for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-  for (int i = 0; i < 2 * C::CB; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-  }
-#endif
+      for (int cb = 0; cb < C::CB; ++cb)
+        acc[cb] = mfma32(ld16(VTs + (32 * cb + lr) * 64 + 8 * ((4 * u + 2 * s2 + hf) ^ tsw)), pb[u][s2], acc[cb]);
 }
 
 template <int D, bool CAUSAL, bool SPLIT>
-__global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(FwdCfg<D>::THREADS, 1) void fwd_bf16_kernel(FwdArgs a) {
   using C = FwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 lds[2 * C::STAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 stages[C::NSTAGE * C::STAGE];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
@@ -270,64 +191,55 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   const int qt = a.num_qtiles - 1 - (item / a.num_splits) % a.num_qtiles;
   const int bh = item / (a.num_splits * a.num_qtiles);
 
-  const int q0 = qt * kBM;
+  const int q0 = qt * C::BM;
   const int row = q0 + wave * 32 + lr;  // this lane's query row
   const __bf16* Qh = a.q + (size_t)bh * a.Tq * D;
-  const __bf16* Kh = a.k + (size_t)bh * a.Tk * D;
-  const __bf16* Vh = a.v + (size_t)bh * a.Tk * D;
 
   int kbeg = 0, kend = a.Tk;
   if (SPLIT) {
     kbeg = split * a.keys_per_split;
     kend = min(a.Tk, kbeg + a.keys_per_split);
   }
-  if (CAUSAL) kend = min(kend, q0 + kBM);
-  const int ntiles = kend > kbeg ? (kend - kbeg + kBN - 1) / kBN : 0;
+  if (CAUSAL) kend = min(kend, q0 + C::BM);
+  const int ntiles = kend > kbeg ? (kend - kbeg + C::BN - 1) / C::BN : 0;
   // end of the keys this wave's rows may see (causal): whole tiles past it are
   // skipped
   const int wave_kend = CAUSAL ? min(kend, q0 + wave * 32 + 32) : kend;
   const int wave_row0 = q0 + wave * 32;
 
   // Q fragments (B operand of S^T = K Q^T): lane holds Q[row][16*ks + 8*hf + 0..7]
-  bf16x8 qf[C::KS];
+  bf16x8 qf[8];
   {
-    const bool ok = row < a.Tq;
+    const int qr = min(row, a.Tq - 1);
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      u32x4 t = ok ? *reinterpret_cast<const u32x4*>(Qh + (size_t)row * D + 16 * ks + 8 * hf)
-                   : u32x4{0u, 0u, 0u, 0u};
-      qf[ks] = __builtin_bit_cast(bf16x8, t);
-    }
+    for (int ks = 0; ks < C::KS; ++ks) qf[ks] = ld16(Qh + (size_t)qr * D + 16 * ks + 8 * hf);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) settle(qf[ks]);
   }
 
-  f32x16 acc[C::CB];
+  f32x16 acc[4];
 #pragma unroll
   for (int cb = 0; cb < C::CB; ++cb) acc[cb] = f32x16{};
   float m_ref = -INFINITY;  // reference max of scaled scores, log2 units
   float l_run = 0.f;        // this lane's share of the running sum
   const float c = a.scale_log2;
 
-  TileRegs<D> tr;
-  if (ntiles > 0) {
-    load_tile<D>(Kh, Vh, kbeg, kend, tid, tr);
-    store_tile<D>(lds, tid, tr);
-  }
-  __syncthreads();
-
+  auto stage = [&](int t) { return stages + (t % C::NSTAGE) * C::STAGE; };
+  for (int t = 0; t < C::AHEAD && t < ntiles; ++t) fwd_issue<D>(a, bh, kbeg + t * C::BN, stage(t), wave, lane);
+  static_assert(C::AHEAD == 3, "the waits below cover up to 2 later tiles");
   for (int t = 0; t < ntiles; ++t) {
-    const int key0 = kbeg + t * kBN;
-    const __bf16* Ks = lds + (t & 1) * C::STAGE;
-    const __bf16* Vt = Ks + C::KTILE;
-    const bool more = t + 1 < ntiles;
-    if (more) load_tile<D>(Kh, Vh, key0 + kBN, kend, tid, tr);
-
+    // this wave's copies of tiles t+1, t+2 may still be in flight
+    const int later = min(C::AHEAD - 1, ntiles - 1 - t);
+    if (later >= 2) wait_vm<2 * C::VM>();
+    else if (later == 1) wait_vm<C::VM>();
+    else wait_vm<0>();
+    barrier();
+    if (t + C::AHEAD < ntiles) fwd_issue<D>(a, bh, kbeg + (t + C::AHEAD) * C::BN, stage(t + C::AHEAD), wave, lane);
+    const int key0 = kbeg + t * C::BN;
     if (key0 < wave_kend) {
-      const bool need_mask = (key0 + kBN > kend) || (CAUSAL && key0 + kBN - 1 > wave_row0);
-      fwd_tile<D>(Ks, Vt, qf, acc, m_ref, l_run, c, lr, hf, need_mask, key0 + 4 * hf, kend, row, CAUSAL);
+      const bool need_mask = (key0 + C::BN > kend) || (CAUSAL && key0 + C::BN - 1 > wave_row0);
+      fwd_tile<D>(stage(t), qf, acc, m_ref, l_run, c, lane, need_mask, key0, kend, row, CAUSAL);
     }
-
-    if (more) store_tile<D>(lds + ((t + 1) & 1) * C::STAGE, tid, tr);
-    __syncthreads();
   }
 
   // ---- epilogue ------------------------------------------------------------------
@@ -408,7 +320,7 @@ template <int D, bool CAUSAL, bool SPLIT>
 hipError_t launch_fwd(const FwdArgs& args, hipStream_t stream) {
   const int n = args.BH * args.num_qtiles * args.num_splits;
   prof_begin(0, stream);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, SPLIT>), dim3(n), dim3(kFwdThreads), 0, stream, args);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, SPLIT>), dim3(n), dim3(FwdCfg<D>::THREADS), 0, stream, args);
   prof_end(0, stream);
   return hipGetLastError();
 }
@@ -417,6 +329,29 @@ template <int D>
 hipError_t fwd_dispatch(const FwdArgs& args, bool causal, bool split, hipStream_t stream) {
   if (causal) return split ? launch_fwd<D, true, true>(args, stream) : launch_fwd<D, true, false>(args, stream);
   return split ? launch_fwd<D, false, true>(args, stream) : launch_fwd<D, false, false>(args, stream);
+}
+
+constexpr int kBM = 256;  // FwdCfg<D>::BM for both head dims
+constexpr int kBN = 64;
+static_assert(FwdCfg<64>::BM == kBM && FwdCfg<128>::BM == kBM && FwdCfg<128>::BN == kBN, "tile sizes");
+
+struct FwdLayout {
+  size_t vt, part_acc, part_ml, total;
+};
+
+FwdLayout fwd_layout(int BH, int Tq, int Tk, int d, int num_splits) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t tk_pad = (size_t)(Tk + kBN - 1) / kBN * kBN;
+  FwdLayout L;
+  L.vt = 0;
+  L.part_acc = up((size_t)BH * d * tk_pad * 2);
+  L.part_ml = L.part_acc;
+  L.total = L.part_acc;
+  if (num_splits > 1) {
+    L.part_ml = up(L.part_acc + (size_t)num_splits * BH * Tq * d * sizeof(float));
+    L.total = up(L.part_ml + (size_t)num_splits * BH * Tq * 2 * sizeof(float));
+  }
+  return L;
 }
 
 }  // namespace
@@ -439,33 +374,48 @@ int fwd_bf16_num_splits(int BH, int Tq, int Tk, int causal, int requested) {
   return s;
 }
 
-size_t fwd_bf16_workspace_bytes(int BH, int Tq, int d, int num_splits) {
-  if (num_splits <= 1) return 0;
-  return (size_t)num_splits * BH * Tq * (d + 2) * sizeof(float);
+size_t fwd_bf16_workspace_bytes(int BH, int Tq, int Tk, int d, int num_splits) {
+  return fwd_layout(BH, Tq, Tk, d, num_splits).total;
 }
 
 hipError_t fwd_bf16_launch(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Tq,
                            int Tk, int d, float scale, int causal, int num_splits, void* workspace,
                            hipStream_t stream) {
+  const FwdLayout L = fwd_layout(BH, Tq, Tk, d, num_splits);
+  char* ws = static_cast<char*>(workspace);
   FwdArgs args;
   args.q = static_cast<const __bf16*>(q);
   args.k = static_cast<const __bf16*>(k);
-  args.v = static_cast<const __bf16*>(v);
+  args.vt = reinterpret_cast<const __bf16*>(ws + L.vt);
   args.o = static_cast<__bf16*>(o);
   args.lse = lse;
   args.BH = BH;
   args.Tq = Tq;
   args.Tk = Tk;
+  args.Tk_pad = (Tk + kBN - 1) / kBN * kBN;
   args.num_qtiles = (Tq + kBM - 1) / kBM;
   args.num_splits = num_splits;
   const int kblocks = (Tk + kBN - 1) / kBN;
   args.keys_per_split = ((kblocks + num_splits - 1) / num_splits) * kBN;
   args.scale_log2 = scale * kLog2e;
   const bool split = num_splits > 1;
-  args.part_acc = split ? static_cast<float*>(workspace) : nullptr;
-  args.part_ml = split ? args.part_acc + (size_t)num_splits * BH * Tq * d : nullptr;
-  hipError_t e = (d == 128) ? fwd_dispatch<128>(args, causal != 0, split, stream)
-                            : fwd_dispatch<64>(args, causal != 0, split, stream);
+  args.part_acc = split ? reinterpret_cast<float*>(ws + L.part_acc) : nullptr;
+  args.part_ml = split ? reinterpret_cast<float*>(ws + L.part_ml) : nullptr;
+
+  // V^T for the A operand of a += V^T P^T
+  prof_begin(1, stream);
+  if (d == 128)
+    hipLaunchKernelGGL(transpose_rows_kernel<128>, dim3(args.Tk_pad / 64, BH), dim3(256), 0, stream,
+                       static_cast<const __bf16*>(v), reinterpret_cast<__bf16*>(ws + L.vt), Tk, args.Tk_pad);
+  else
+    hipLaunchKernelGGL(transpose_rows_kernel<64>, dim3(args.Tk_pad / 64, BH), dim3(256), 0, stream,
+                       static_cast<const __bf16*>(v), reinterpret_cast<__bf16*>(ws + L.vt), Tk, args.Tk_pad);
+  prof_end(1, stream);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  e = (d == 128) ? fwd_dispatch<128>(args, causal != 0, split, stream)
+                 : fwd_dispatch<64>(args, causal != 0, split, stream);
   if (e != hipSuccess || !split) return e;
   const int rows = BH * Tq;
   const int blocks = (rows + 3) / 4;

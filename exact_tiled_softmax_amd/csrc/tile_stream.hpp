@@ -1,0 +1,112 @@
+// Internal helpers for streaming bf16 tiles through LDS on gfx950: the
+// direct-to-LDS copy, its waits, a barrier, the LDS swizzle, and the
+// transposed copy of K or V that the MFMA operand order needs.  Not part of
+// the ABI.
+#pragma once
+
+#include "attn_common.hpp"
+
+namespace attn {
+namespace {
+
+typedef __attribute__((address_space(3))) const void lds_cvoid;
+
+// One wave copies 16 bytes per lane from `src` (per lane) to LDS; lane l's
+// bytes land at lds_base + 16*l (lds_base must be the same in every lane).
+// Issued as inline assembly so that the compiler neither reorders LDS
+// accesses across it nor adds waits of its own for it: every copy is waited
+// for explicitly (wait_vm) before a barrier that publishes the tile.  The
+// LDS base goes through M0, which the compiler reserves but keeps no value
+// in for any instruction these kernels use (the generated code writes M0
+// only here), so clobbering it is safe.
+__device__ __forceinline__ void dma16(const __bf16* src, const __bf16* lds_base) {
+  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_cvoid*)lds_base));
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Workgroup barrier after this wave's LDS reads and writes have completed;
+// it also keeps the compiler from moving memory accesses across it.  Tile
+// copies into LDS are waited for separately (wait_vm) before it.
+__device__ __forceinline__ void barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ __forceinline__ bf16x8 ld16(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+// Make the compiler complete a register load here, before the tile copies
+// that follow are issued: its own waits count only its own loads, so a wait
+// for this value inside the tile loop would also drain the copies.
+__device__ __forceinline__ void settle(const bf16x8& x) { asm volatile("" ::"v"(__builtin_bit_cast(u32x4, x))); }
+__device__ __forceinline__ void settle(float x) { asm volatile("" ::"v"(x)); }
+
+// Swizzle of a row-major LDS tile with CPR 16-byte chunks per row: logical
+// chunk c of row r is stored at chunk r*CPR + (c ^ swz<CPR>(r)).  For every
+// CPR, 16 consecutive rows read at one logical chunk hit 16 different
+// 16-byte bank groups (a 16-byte read of 32 rows has no bank conflict), and
+// for CPR 8 and 16 the 4 rows x 4 chunks that half a wave touches in a
+// transposing read (rows 4a..4a+3, chunks 4m..4m+3) are 16 different bank
+// groups as well.
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+  static_assert(CPR == 4 || CPR == 8 || CPR == 16, "chunks per row");
+  if constexpr (CPR == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else if constexpr (CPR == 8) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  else return (r >> 2) & 3;
+}
+
+// Row of a 16-row group that the transposed copies store at position p
+// (0..15).  An MFMA accumulator gives lane half h the rows 4h..4h+3 and
+// 8+4h..8+4h+3 of each 16-row group, and an operand read takes 8 consecutive
+// positions, so position 8h+e holds row (e < 4 ? 4h+e : 8+4h+e-4).
+__device__ __forceinline__ int group_row(int p) {
+  const int h = (p >> 3) & 1, e = p & 7;
+  return (e < 4) ? 4 * h + e : 8 + 4 * h + (e - 4);
+}
+
+// Transposed copy [d][Tpad] of a row-major [T][d] bf16 tensor (per head),
+// rows of each 16-row group stored in group_row order, zero past T.
+// One 64-row block of one head per workgroup.
+// out[bh][c][tpos] = in[bh][t][c] with t = 16*(tpos/16) + group_row(tpos%16),
+// zero for t >= T.
+template <int D>
+__global__ __launch_bounds__(256) void transpose_rows_kernel(const __bf16* __restrict__ in_all,
+                                                            __bf16* __restrict__ out_all, int T, int Tpad) {
+  constexpr int STR = D + 8;
+  constexpr int CPR = D / 8;
+  __shared__ __attribute__((aligned(16))) __bf16 tile[64 * STR];
+  const int bh = blockIdx.y;
+  const int t0 = blockIdx.x * 64;
+  const __bf16* in = in_all + (size_t)bh * T * D;
+  __bf16* out = out_all + (size_t)bh * D * Tpad;
+  for (int c = threadIdx.x; c < 64 * CPR; c += 256) {
+    const int r = c / CPR, col = (c % CPR) * 8;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (t0 + r < T) x = *reinterpret_cast<const u32x4*>(in + (size_t)(t0 + r) * D + col);
+    *reinterpret_cast<u32x4*>(tile + r * STR + col) = x;
+  }
+  __syncthreads();
+  const uint16_t* ts = reinterpret_cast<const uint16_t*>(tile);
+  for (int it = threadIdx.x; it < D * 8; it += 256) {
+    const int c = it / 8, m = it % 8;  // output row c, positions 8m..8m+7
+    unsigned w[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const int p0 = 8 * m + e, p1 = p0 + 1;
+      const int r0 = (p0 & ~15) + group_row(p0 & 15), r1 = (p1 & ~15) + group_row(p1 & 15);
+      w[e / 2] = (unsigned)ts[r0 * STR + c] | ((unsigned)ts[r1 * STR + c] << 16);
+    }
+    const u32x4 v = {w[0], w[1], w[2], w[3]};
+    *reinterpret_cast<u32x4*>(out + (size_t)c * Tpad + t0 + 8 * m) = v;
+  }
+}
+
+}  // namespace
+}  // namespace attn

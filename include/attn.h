@@ -45,10 +45,10 @@
  * Stream.   `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *           enqueue work on it and never synchronise; kernel faults surface at
  *           the caller's next synchronisation on that stream.
- * Workspace. attn_bwd and (for long key ranges) attn_fwd need scratch memory
- *           (fp32 dQ accumulator, row sums D, split partial states).  The
- *           library takes it with hipMallocAsync on `stream` and returns it
- *           with hipFreeAsync on the same stream, so its lifetime is
+ * Workspace. attn_fwd and attn_bwd need scratch memory (transposed copies
+ *           of V or K, row statistics, split partial states).  The library
+ *           takes it with hipMallocAsync on `stream` and returns it with
+ *           hipFreeAsync on the same stream, so its lifetime is
  *           stream-ordered and no state persists between calls.
  * Errors.   Return 0 on success or a negative ATTN_ERR_* code.  Argument
  *           checks happen before any HIP call, so an invalid call has no
@@ -78,6 +78,8 @@ extern "C" {
  * statistics are fp32; P is rounded to bf16 before the P V product.
  * Supported: d == dv, d in {64, 128}; otherwise ATTN_ERR_UNSUPPORTED.
  * B, H, Tq, Tk >= 1 (any value; ragged tails are masked).
+ * Workspace: a transposed copy of V (B*H*dv*Tk*2 bytes, Tk rounded up to 64)
+ * plus, with key splits, the partial states.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int H, int Tq, int Tk, int d, int dv, float scale, int causal,
@@ -156,7 +158,7 @@ int attn_bwd_f32(const float* q, const float* k, const float* v, const float* o,
  *       an unknown kind or null pointers, ATTN_ERR_HIP if an event fails.
  */
 #define ATTN_KERNEL_FWD 0            /* forward main kernel */
-#define ATTN_KERNEL_FWD_COMBINE 1    /* merge of key-split partial states */
+#define ATTN_KERNEL_FWD_AUX 1        /* forward: transposed copy of V, merge of key-split states */
 #define ATTN_KERNEL_BWD_PREP 2       /* D = rowsum(dO o O), LSE*log2(e), transposed K */
 #define ATTN_KERNEL_BWD_DKDV 3       /* backward: dK and dV */
 #define ATTN_KERNEL_BWD_DQ 4         /* backward: dQ */
