@@ -78,8 +78,9 @@ def kernel_source_digest(files):
     return h.hexdigest()[:16]
 
 
-KERNEL_SOURCES = {"fwd": ["fwd_bf16.hip", "attn_common.hpp"], "bwd_dkdv": ["bwd_bf16.hip", "attn_common.hpp"],
-                  "bwd_dq": ["bwd_bf16.hip", "attn_common.hpp"]}
+KERNEL_SOURCES = {"fwd": ["fwd_bf16.hip", "attn_common.hpp", "tile_stream.hpp"],
+                  "bwd_dkdv": ["bwd_bf16.hip", "attn_common.hpp", "tile_stream.hpp"],
+                  "bwd_dq": ["bwd_bf16.hip", "attn_common.hpp", "tile_stream.hpp"]}
 KERNEL_SYMBOL = {"fwd": "fwd_bf16_kernel", "bwd_dkdv": "bwd_dkdv_kernel", "bwd_dq": "bwd_dq_kernel"}
 
 

@@ -60,6 +60,7 @@ struct FwdCfg {
   static constexpr int STAGE = 2 * TILE;
   static constexpr int NSTAGE = 4;
   static constexpr int AHEAD = NSTAGE - 1;               // tiles in flight ahead of the compute
+  static constexpr int WG_PER_CU = 1;
   static_assert(PER_WAVE >= 1 && 2 * PER_TENSOR == PER_WAVE * WAVES, "tile copy split");
 };
 
@@ -176,7 +177,7 @@ __device__ __forceinline__ void fwd_tile(const __bf16* stg, const bf16x8 (&qf)[8
 }
 
 template <int D, bool CAUSAL, bool SPLIT>
-__global__ __launch_bounds__(FwdCfg<D>::THREADS, 1) void fwd_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(FwdCfg<D>::THREADS, FwdCfg<D>::WG_PER_CU) void fwd_bf16_kernel(FwdArgs a) {
   using C = FwdCfg<D>;
   __shared__ __attribute__((aligned(1024))) __bf16 stages[C::NSTAGE * C::STAGE];
 
@@ -226,12 +227,12 @@ __global__ __launch_bounds__(FwdCfg<D>::THREADS, 1) void fwd_bf16_kernel(FwdArgs
 
   auto stage = [&](int t) { return stages + (t % C::NSTAGE) * C::STAGE; };
   for (int t = 0; t < C::AHEAD && t < ntiles; ++t) fwd_issue<D>(a, bh, kbeg + t * C::BN, stage(t), wave, lane);
-  static_assert(C::AHEAD == 3, "the waits below cover up to 2 later tiles");
+  static_assert(C::AHEAD >= 1 && C::AHEAD <= 3, "the waits below cover up to 2 later tiles");
   for (int t = 0; t < ntiles; ++t) {
-    // this wave's copies of tiles t+1, t+2 may still be in flight
+    // this wave's copies of tiles t+1 .. t+AHEAD-1 may still be in flight
     const int later = min(C::AHEAD - 1, ntiles - 1 - t);
-    if (later >= 2) wait_vm<2 * C::VM>();
-    else if (later == 1) wait_vm<C::VM>();
+    if (C::AHEAD >= 3 && later >= 2) wait_vm<2 * C::VM>();
+    else if (C::AHEAD >= 2 && later == 1) wait_vm<C::VM>();
     else wait_vm<0>();
     barrier();
     if (t + C::AHEAD < ntiles) fwd_issue<D>(a, bh, kbeg + (t + C::AHEAD) * C::BN, stage(t + C::AHEAD), wave, lane);
@@ -331,7 +332,7 @@ hipError_t fwd_dispatch(const FwdArgs& args, bool causal, bool split, hipStream_
   return split ? launch_fwd<D, false, true>(args, stream) : launch_fwd<D, false, false>(args, stream);
 }
 
-constexpr int kBM = 256;  // FwdCfg<D>::BM for both head dims
+constexpr int kBM = FwdCfg<128>::BM;  // the same for both head dims
 constexpr int kBN = 64;
 static_assert(FwdCfg<64>::BM == kBM && FwdCfg<128>::BM == kBM && FwdCfg<128>::BN == kBN, "tile sizes");
 
