@@ -32,12 +32,24 @@ full score rows materialised:
   exp(score - new max)).  The step's own formulas are missing from the page
   text; this reading is pinned by the page's third worked example.  It exists
   to pin the dense oracle (block-size invariance), never as the oracle itself.
+* Partial state and merge.  The exact (m, l, a) of one key range (m its row
+  maximum, l and a its exp-weighted sum and value sum), with global query and
+  key offsets for the causal mask, and the rule that combines such states:
+  "The Hidden Recurrence in Softmax Attention", section "Chunk-wise Mode with
+  Online Softmax Re-scale" (each state rescaled by exp(m_s - max), summed;
+  O = a / l, LSE = max + ln l).
+* Gradient of the log-sum-exp.  When a caller also differentiates LSE, its
+  upstream gradient dLSE adds dLSE o P to dS, since d LSE_i / d S_ij = P_ij
+  ("Flash Attention Backward Pass", which treats l as a smooth function of the
+  scores that the gradient flows through).  Equivalently the row term
+  ROW_SUM(dO o O) is replaced by ROW_SUM(dO o O) - dLSE.
 
 Pins (tests/test_oracle_pins.py): the three worked examples of "Tiled
 attention with an online softmax", section "Examples"; block-size invariance
 to 1e-9 (section "Constraints"); closed forms and invariants; central finite
-differences of the backward; and an independent library routine (torch CPU
-autograd in float64).
+differences of the backward, also with a dLSE input; an independent library
+routine (torch CPU autograd in float64, with and without dLSE); and merged
+key-range states against the dense forward of the whole range.
 """
 from __future__ import annotations
 
@@ -110,7 +122,7 @@ def dense_forward(q, k, v, scale, causal=False, row_chunk=2048):
     return o.reshape(lead + o.shape[-2:]), lse.reshape(lead + lse.shape[-1:])
 
 
-def _head_backward(q, k, v, dout, scale, causal, row_chunk):
+def _head_backward(q, k, v, dout, scale, causal, row_chunk, dlse=None):
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
@@ -125,18 +137,25 @@ def _head_backward(q, k, v, dout, scale, causal, row_chunk):
         # "attention backprop", "Gradient of S": dS = dP o P - ROW_SUM(dO o O) o P
         rowsum = np.sum(do * o, axis=1, keepdims=True)
         ds = dp * p - rowsum * p
+        if dlse is not None:
+            # an upstream gradient on LSE_i = m_i + ln l_i flows through l
+            # ("The Hidden Recurrence in Softmax Attention", "Flash Attention
+            # Backward Pass"): d LSE_i / d S_ij = P_ij
+            ds = ds + dlse[r0:r1, None] * p
         # "attention backprop", "Gradient of Q and K", times the chain-rule scale
         dq[r0:r1] = scale * (ds @ k)
         dk += scale * (ds.T @ q[r0:r1])
     return dq, dk, dv
 
 
-def dense_backward(q, k, v, dout, scale, causal=False, row_chunk=2048):
-    """Gradients (dq, dk, dv) of L = sum(dout * O) for O = dense_forward(...).
+def dense_backward(q, k, v, dout, scale, causal=False, row_chunk=2048, dlse=None):
+    """Gradients (dq, dk, dv) of L = sum(dout * O) (+ sum(dlse * LSE) when
+    `dlse` [..., Tq] is given) for (O, LSE) = dense_forward(...).
 
     Recomputes P from the inputs in float64 (rows complete).  Shapes as in
     dense_forward; dout has O's shape."""
     q, k, v, dout = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
+    dlf = None if dlse is None else _as_f64(dlse).reshape((-1, q.shape[-2]))
     lead = q.shape[:-2]
     qf = q.reshape((-1,) + q.shape[-2:])
     kf = k.reshape((-1,) + k.shape[-2:])
@@ -146,8 +165,54 @@ def dense_backward(q, k, v, dout, scale, causal=False, row_chunk=2048):
     dk = np.empty_like(kf)
     dv = np.empty_like(vf)
     for n in range(qf.shape[0]):
-        dq[n], dk[n], dv[n] = _head_backward(qf[n], kf[n], vf[n], df[n], scale, causal, row_chunk)
+        dq[n], dk[n], dv[n] = _head_backward(qf[n], kf[n], vf[n], df[n], scale, causal, row_chunk,
+                                             None if dlf is None else dlf[n])
     return dq.reshape(q.shape), dk.reshape(k.shape), dv.reshape(v.shape)
+
+
+# --- Partial states of key ranges and their merge -----------------------------
+
+def attention_state(q, k, v, scale, causal=False, q_offset=0, k_offset=0):
+    """The state (m, l, acc) of each query row over one key range, in the
+    sense of "Tiled attention with an online softmax", section "Task": m_i
+    the largest allowed scaled score, l_i = sum_j exp(s_ij - m_i) and
+    acc_i = sum_j exp(s_ij - m_i) v_j over the allowed keys j.  With
+    `causal`, key j of this range is blocked for query i when
+    k_offset + j > q_offset + i (global positions).  A row with no allowed
+    key has m = -inf, l = 0, acc = 0.  Shapes as in dense_forward; returns
+    (m [..., Tq], l [..., Tq], acc [..., Tq, dv])."""
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    s = scale * (q @ np.swapaxes(k, -1, -2))
+    if causal:
+        s = np.where(causal_blocked(s.shape[-2], s.shape[-1], row0=q_offset, col0=k_offset), NEG_INF, s)
+    m = np.max(s, axis=-1)
+    mu = np.where(np.isneginf(m), 0.0, m)
+    e = np.exp(s - mu[..., None])
+    return m, np.sum(e, axis=-1), e @ v
+
+
+def merge_states(ms, ls, accs):
+    """(O, LSE) of the union of key ranges from their states (sequences of
+    m [..., Tq], l [..., Tq], acc [..., Tq, dv]): every state is rescaled to
+    the common max M = max_s m_s ("The Hidden Recurrence in Softmax
+    Attention", section "Chunk-wise Mode with Online Softmax Re-scale"),
+    l = sum_s exp(m_s - M) l_s, acc = sum_s exp(m_s - M) acc_s, O = acc / l,
+    LSE = M + ln l (O = 0 and LSE = -inf where l = 0)."""
+    ms = [_as_f64(x) for x in ms]
+    M = ms[0]
+    for x in ms[1:]:
+        M = np.maximum(M, x)
+    mu = np.where(np.isneginf(M), 0.0, M)
+    l = np.zeros_like(mu)
+    acc = np.zeros_like(_as_f64(accs[0]))
+    for m_s, l_s, a_s in zip(ms, ls, accs):
+        w = np.exp(m_s - mu)
+        l = l + w * _as_f64(l_s)
+        acc = acc + w[..., None] * _as_f64(a_s)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        o = np.where(l[..., None] > 0, acc / np.where(l > 0, l, 1.0)[..., None], 0.0)
+        lse = np.where(l > 0, mu + np.log(np.where(l > 0, l, 1.0)), NEG_INF)
+    return o, lse
 
 
 # --- Sampled outputs for large shapes ----------------------------------------

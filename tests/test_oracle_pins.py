@@ -133,6 +133,90 @@ def pin_torch(mod):
     return ok
 
 
+def _loss_dlse(mod, q, k, v, do, dl, scale, causal):
+    o, lse = mod.dense_forward(q, k, v, scale, causal)
+    return float(np.sum(do * o) + np.sum(dl * lse))
+
+
+def pin_fd_dlse(mod, h=1e-6):
+    """The dLSE term of the backward against central finite differences of
+    L = sum(dO o O) + sum(dLSE o LSE) through the oracle forward."""
+    for seed, tq, tk, d, dv, causal in [(31, 3, 4, 3, 2, True), (32, 2, 3, 2, 3, False)]:
+        r = _rng(seed)
+        q, k, v = r.standard_normal((tq, d)), r.standard_normal((tk, d)), r.standard_normal((tk, dv))
+        do, dl = r.standard_normal((tq, dv)), r.standard_normal((tq,))
+        scale = 0.7
+        grads = mod.dense_backward(q, k, v, do, scale, causal, dlse=dl)
+        for x, gx in zip((q, k, v), grads):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                keep = x[idx]
+                x[idx] = keep + h
+                lp = _loss_dlse(mod, q, k, v, do, dl, scale, causal)
+                x[idx] = keep - h
+                lm = _loss_dlse(mod, q, k, v, do, dl, scale, causal)
+                x[idx] = keep
+                num[idx] = (lp - lm) / (2 * h)
+            if np.max(np.abs(num - gx)) > 1e-7 * max(1.0, float(np.max(np.abs(num)))):
+                return False
+    return True
+
+
+def pin_torch_dlse(mod):
+    """Gradients of sum(dO o O) + sum(dLSE o LSE) from torch float64 autograd
+    (SDPA for O, logsumexp of the masked scores for LSE)."""
+    for seed, tq, tk, d, dv, causal in [(41, 12, 19, 6, 5, True), (42, 9, 9, 4, 4, False)]:
+        r = _rng(seed)
+        q, k, v = r.standard_normal((tq, d)), r.standard_normal((tk, d)), r.standard_normal((tk, dv))
+        do, dl = r.standard_normal((tq, dv)), r.standard_normal((tq,))
+        scale = 1 / np.sqrt(d)
+        tq_, tk_, tv_ = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+        o = torch.nn.functional.scaled_dot_product_attention(tq_[None], tk_[None], tv_[None], is_causal=causal,
+                                                              scale=scale)[0]
+        sc = scale * (tq_ @ tk_.T)
+        if causal:
+            sc = sc.masked_fill(torch.ones(sc.shape, dtype=torch.bool).triu(1), float("-inf"))
+        loss = torch.sum(torch.tensor(do) * o) + torch.sum(torch.tensor(dl) * torch.logsumexp(sc, dim=-1))
+        loss.backward()
+        mine = mod.dense_backward(q, k, v, do, scale, causal, dlse=dl)
+        for a, b in zip(mine, (tq_.grad.numpy(), tk_.grad.numpy(), tv_.grad.numpy())):
+            if not np.allclose(a, b, rtol=1e-11, atol=1e-11):
+                return False
+    return True
+
+
+def pin_state_merge(mod):
+    """States of key ranges merged by the rescale rule give the dense forward
+    of the whole key range (an independent computation), with causal offsets
+    on both the query and the key side; and one range's state is the page's
+    online step applied to an empty state."""
+    for seed, causal in [(51, False), (52, True)]:
+        r = _rng(seed)
+        t_full, q_off, tq, d, dv = 40, 23, 17, 6, 5
+        qf = r.standard_normal((t_full, d))
+        k, v = r.standard_normal((t_full, d)), r.standard_normal((t_full, dv))
+        q = qf[q_off:q_off + tq]
+        scale = 0.9
+        o_ref, lse_ref = mod.dense_forward(qf, k, v, scale, causal)
+        o_ref, lse_ref = o_ref[q_off:q_off + tq], lse_ref[q_off:q_off + tq]
+        cuts = [0, 11, 29, t_full]
+        states = [mod.attention_state(q, k[a:b], v[a:b], scale, causal, q_offset=q_off, k_offset=a)
+                  for a, b in zip(cuts[:-1], cuts[1:])]
+        o, lse = mod.merge_states([x[0] for x in states], [x[1] for x in states], [x[2] for x in states])
+        if not (np.allclose(o, o_ref, rtol=0, atol=1e-12) and np.allclose(lse, lse_ref, rtol=0, atol=1e-12)):
+            return False
+        a, b = cuts[1], cuts[2]
+        s = scale * (q @ k[a:b].T)
+        if causal:
+            s = np.where(mod.causal_blocked(tq, b - a, row0=q_off, col0=a), -np.inf, s)
+        m1, l1, a1 = mod.online_softmax_step(np.full(tq, -np.inf), np.zeros(tq), np.zeros((tq, dv)), s, v[a:b])
+        m2, l2, a2 = states[1]
+        if not (np.array_equal(m1, m2) and np.allclose(l1, l2, rtol=1e-14, atol=0)
+                and np.allclose(a1, a2, rtol=1e-13, atol=1e-14)):
+            return False
+    return True
+
+
 def pin_block_invariance(mod):
     ok = True
     for seed, tq, tk, d, dv in [(21, 64, 64, 64, 64), (22, 5, 37, 3, 9), (23, 37, 5, 8, 2), (24, 1, 1, 1, 1)]:
@@ -372,6 +456,11 @@ MUTANTS = {
     "tiled_last_block_dropped": ("stop = min(tk, start + block_size)", "stop = start + block_size\n        if stop > tk:\n            break"),
     "dense_row_norm_missing": ("p = np.where(l > 0, e / np.where(l > 0, l, 1.0), 0.0)", "p = e"),
     "transposed_pv": ("o[r0:r1] = p @ v", "o[r0:r1] = (p @ v)[:, ::-1]"),
+    "dlse_wrong_sign": ("ds = ds + dlse[r0:r1, None] * p", "ds = ds - dlse[r0:r1, None] * p"),
+    "state_ignores_offsets": ("causal_blocked(s.shape[-2], s.shape[-1], row0=q_offset, col0=k_offset)",
+                              "causal_blocked(s.shape[-2], s.shape[-1])"),
+    "merge_weight_inverted": ("w = np.exp(m_s - mu)", "w = np.exp(mu - m_s)"),
+    "merge_l_unweighted": ("l = l + w * _as_f64(l_s)", "l = l + _as_f64(l_s)"),
 }
 
 
@@ -394,6 +483,9 @@ def _all_pins_pass(mod, g):
         lambda: pin_blocked_row(mod),
         lambda: pin_torch(mod),
         lambda: pin_fd(mod),
+        lambda: pin_state_merge(mod),
+        lambda: pin_torch_dlse(mod),
+        lambda: pin_fd_dlse(mod),
     ]
     for c in checks:
         try:
@@ -403,6 +495,23 @@ def _all_pins_pass(mod, g):
         except Exception:
             return False
     return True
+
+
+def test_dlse_backward_matches_finite_differences_and_torch():
+    assert pin_fd_dlse(ao)
+    assert pin_torch_dlse(ao)
+
+
+def test_merged_key_range_states_equal_dense_forward():
+    assert pin_state_merge(ao)
+
+
+def test_state_of_fully_blocked_rows_is_empty_and_merges_to_nothing():
+    q, k, v = np.ones((3, 2)), np.ones((4, 2)), np.ones((4, 3))
+    m, l, acc = ao.attention_state(q, k, v, 1.0, causal=True, q_offset=0, k_offset=10)
+    assert np.all(np.isneginf(m)) and np.all(l == 0) and np.all(acc == 0)
+    o, lse = ao.merge_states([m], [l], [acc])
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
 
 
 def test_unmutated_oracle_passes_every_pin(golden):
