@@ -21,8 +21,9 @@ ATTN_ERR_INVALID_ARG = -1
 ATTN_ERR_UNSUPPORTED = -2
 ATTN_ERR_HIP = -3
 
-EXPORTED = ("attn_fwd", "attn_fwd_splits", "attn_bwd", "attn_fwd_f32", "attn_bwd_f32", "attn_strerror",
-            "attn_last_hip_error", "attn_profile_start", "attn_profile_stop", "attn_profile_query")
+EXPORTED = ("attn_fwd", "attn_fwd_splits", "attn_bwd", "attn_bwd_dlse", "attn_fwd_state", "attn_merge_states",
+            "attn_fwd_f32", "attn_bwd_f32", "attn_strerror", "attn_last_hip_error", "attn_profile_start",
+            "attn_profile_stop", "attn_profile_query")
 
 # kernel kinds of attn_profile_query (include/attn.h)
 KERNEL_FWD = 0
@@ -54,9 +55,13 @@ def load() -> ctypes.CDLL:
     lib.attn_fwd.argtypes = [P, P, P, P, P, *dims, P]
     lib.attn_fwd_splits.argtypes = [P, P, P, P, P, *dims, I, P]
     lib.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, *dims, P]
+    lib.attn_bwd_dlse.argtypes = [P, P, P, P, P, P, P, P, P, P, *dims, P]
+    lib.attn_fwd_state.argtypes = [P, P, P, P, P, P, *dims, I, I, P]
+    lib.attn_merge_states.argtypes = [P, P, P, I, P, P, I, I, I, I, P]
     lib.attn_fwd_f32.argtypes = [P, P, P, P, P, *dims, I, P]
     lib.attn_bwd_f32.argtypes = [P, P, P, P, P, P, P, P, P, *dims, P]
-    for fn in ("attn_fwd", "attn_fwd_splits", "attn_bwd", "attn_fwd_f32", "attn_bwd_f32"):
+    for fn in ("attn_fwd", "attn_fwd_splits", "attn_bwd", "attn_bwd_dlse", "attn_fwd_state", "attn_merge_states",
+               "attn_fwd_f32", "attn_bwd_f32"):
         getattr(lib, fn).restype = I
     lib.attn_strerror.argtypes = [I]
     lib.attn_strerror.restype = ctypes.c_char_p
@@ -133,8 +138,9 @@ def fwd(q, k, v, scale=None, causal=False, out=None, lse=None, num_splits=None):
     return out, lse
 
 
-def bwd(q, k, v, o, lse, dout, scale=None, causal=False, dq=None, dk=None, dv=None):
-    """bf16 backward: returns (dq, dk, dv) bf16 with the shapes of q, k, v."""
+def bwd(q, k, v, o, lse, dout, scale=None, causal=False, dq=None, dk=None, dv=None, dlse=None):
+    """bf16 backward: returns (dq, dk, dv) bf16 with the shapes of q, k, v.
+    dlse (optional, fp32 [B,H,Tq]): upstream gradient on the LSE output."""
     lib = load()
     B, H, Tq, Tk, d, dvd = _dims(q, k, v)
     dev = q.device
@@ -148,10 +154,50 @@ def bwd(q, k, v, o, lse, dout, scale=None, causal=False, dq=None, dk=None, dv=No
     dv = torch.empty_like(v) if dv is None else dv
     for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
         _need(t, n, torch.bfloat16, dev)
-    rc = lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
-                      B, H, Tq, Tk, d, dvd, float(scale), int(bool(causal)), _stream(dev))
-    _check("attn_bwd", rc)
+    tail = (_ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), B, H, Tq, Tk, d, dvd, float(scale), int(bool(causal)),
+            _stream(dev))
+    if dlse is None:
+        _check("attn_bwd", lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), *tail))
+    else:
+        _need(dlse, "dlse", torch.float32, dev)
+        _check("attn_bwd_dlse", lib.attn_bwd_dlse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dlse), *tail))
     return dq, dk, dv
+
+
+def fwd_state(q, k, v, scale=None, causal=False, q_offset=0, k_offset=0):
+    """Partial online-softmax state of the keys k, v for the queries q:
+    returns (acc [B,H,Tq,dv] fp32, m [B,H,Tq] fp32 natural-log, l [B,H,Tq] fp32)."""
+    lib = load()
+    B, H, Tq, Tk, d, dv = _dims(q, k, v)
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, torch.bfloat16, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    acc = torch.empty((B, H, Tq, dv), dtype=torch.float32, device=dev)
+    m = torch.empty((B, H, Tq), dtype=torch.float32, device=dev)
+    l = torch.empty((B, H, Tq), dtype=torch.float32, device=dev)
+    rc = lib.attn_fwd_state(_ptr(q), _ptr(k), _ptr(v), _ptr(acc), _ptr(m), _ptr(l), B, H, Tq, Tk, d, dv,
+                            float(scale), int(bool(causal)), int(q_offset), int(k_offset), _stream(dev))
+    _check("attn_fwd_state", rc)
+    return acc, m, l
+
+
+def merge_states(acc, m, l):
+    """Merge n partial states stacked on dim 0 (acc [n,B,H,Tq,dv], m and l
+    [n,B,H,Tq], fp32) into (o [B,H,Tq,dv] bf16, lse [B,H,Tq] fp32)."""
+    lib = load()
+    if acc.dim() != 5 or m.dim() != 4 or l.dim() != 4 or m.shape != acc.shape[:4] or l.shape != m.shape:
+        raise ValueError("acc must be [n,B,H,Tq,dv] and m, l [n,B,H,Tq]")
+    n, B, H, Tq, dv = acc.shape
+    dev = acc.device
+    for t, nm in ((acc, "acc"), (m, "m"), (l, "l")):
+        _need(t, nm, torch.float32, dev)
+    o = torch.empty((B, H, Tq, dv), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, Tq), dtype=torch.float32, device=dev)
+    rc = lib.attn_merge_states(_ptr(acc), _ptr(m), _ptr(l), n, _ptr(o), _ptr(lse), B, H, Tq, dv, _stream(dev))
+    _check("attn_merge_states", rc)
+    return o, lse
 
 
 def fwd_f32(q, k, v, scale=None, causal=False, block_n=0, out=None, lse=None):

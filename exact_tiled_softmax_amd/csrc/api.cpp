@@ -68,6 +68,24 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
 }
 
+int bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse, const float* dlse,
+             const void* dout, void* dq, void* dk, void* dv_grad, int B, int H, int Tq, int Tk, int d, int dv,
+             float scale, int causal, void* stream) {
+  int rc = check_common(q, k, v, o, lse, B, H, Tq, Tk, d, dv, scale);
+  if (rc != ATTN_OK) return rc;
+  if (!dout || !dq || !dk || !dv_grad) return ATTN_ERR_INVALID_ARG;
+  if (!bf16_dims_supported(d, dv)) return ATTN_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int BH = B * H;
+  void* ws = nullptr;
+  hipError_t e = hipMallocAsync(&ws, attn::bwd_bf16_workspace_bytes(BH, Tq, Tk, d), s);
+  if (e != hipSuccess) return hip_fail(e);
+  e = attn::bwd_bf16_launch(q, k, v, o, lse, dlse, dout, dq, dk, dv_grad, BH, Tq, Tk, d, scale, causal, ws, s);
+  hipError_t f = hipFreeAsync(ws, s);
+  if (e == hipSuccess) e = f;
+  return e == hipSuccess ? ATTN_OK : hip_fail(e);
+}
+
 // ---- event profiler ----------------------------------------------------------
 struct Prof {
   std::mutex mu;
@@ -185,18 +203,44 @@ int attn_fwd_splits(const void* q, const void* k, const void* v, void* o, float*
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
              void* dq, void* dk, void* dv_grad, int B, int H, int Tq, int Tk, int d, int dv, float scale, int causal,
              void* stream) {
-  int rc = check_common(q, k, v, o, lse, B, H, Tq, Tk, d, dv, scale);
-  if (rc != ATTN_OK) return rc;
-  if (!dout || !dq || !dk || !dv_grad) return ATTN_ERR_INVALID_ARG;
+  return bwd_impl(q, k, v, o, lse, nullptr, dout, dq, dk, dv_grad, B, H, Tq, Tk, d, dv, scale, causal, stream);
+}
+
+int attn_bwd_dlse(const void* q, const void* k, const void* v, const void* o, const float* lse, const float* dlse,
+                  const void* dout, void* dq, void* dk, void* dv_grad, int B, int H, int Tq, int Tk, int d, int dv,
+                  float scale, int causal, void* stream) {
+  if (!dlse) return ATTN_ERR_INVALID_ARG;
+  return bwd_impl(q, k, v, o, lse, dlse, dout, dq, dk, dv_grad, B, H, Tq, Tk, d, dv, scale, causal, stream);
+}
+
+int attn_fwd_state(const void* q, const void* k, const void* v, float* acc, float* m, float* l, int B, int H, int Tq,
+                   int Tk, int d, int dv, float scale, int causal, int q_offset, int k_offset, void* stream) {
+  if (!q || !k || !v || !acc || !m || !l) return ATTN_ERR_INVALID_ARG;
+  if (!dims_ok(B, H, Tq, Tk, d, dv) || !scale_ok(scale)) return ATTN_ERR_INVALID_ARG;
+  if (q_offset < 0 || k_offset < 0) return ATTN_ERR_INVALID_ARG;
   if (!bf16_dims_supported(d, dv)) return ATTN_ERR_UNSUPPORTED;
+  // blocked iff k_offset + j > q_offset + i, i.e. j > i + diag
+  const long long diag = (long long)q_offset - (long long)k_offset;
+  const long long lim = 1LL << 30;
+  const int diag_c = (int)(diag > lim ? lim : (diag < -lim ? -lim : diag));
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int BH = B * H;
   void* ws = nullptr;
-  hipError_t e = hipMallocAsync(&ws, attn::bwd_bf16_workspace_bytes(BH, Tq, Tk, d), s);
+  hipError_t e = hipMallocAsync(&ws, attn::fwd_bf16_state_workspace_bytes(BH, Tq, Tk, d), s);
   if (e != hipSuccess) return hip_fail(e);
-  e = attn::bwd_bf16_launch(q, k, v, o, lse, dout, dq, dk, dv_grad, BH, Tq, Tk, d, scale, causal, ws, s);
+  e = attn::fwd_bf16_state_launch(q, k, v, acc, m, l, BH, Tq, Tk, d, scale, causal, diag_c, ws, s);
   hipError_t f = hipFreeAsync(ws, s);
   if (e == hipSuccess) e = f;
+  return e == hipSuccess ? ATTN_OK : hip_fail(e);
+}
+
+int attn_merge_states(const float* acc, const float* m, const float* l, int n, void* o, float* lse, int B, int H,
+                      int Tq, int dv, void* stream) {
+  if (!acc || !m || !l || !o || !lse) return ATTN_ERR_INVALID_ARG;
+  if (n < 1 || !dims_ok(B, H, Tq, 1, dv, dv)) return ATTN_ERR_INVALID_ARG;
+  if ((long long)n * B * H * Tq * dv > (1LL << 40)) return ATTN_ERR_INVALID_ARG;
+  if (dv != 64 && dv != 128) return ATTN_ERR_UNSUPPORTED;
+  hipError_t e = attn::merge_states_launch(acc, m, l, n, o, lse, B * H, Tq, dv, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
 }
 

@@ -21,12 +21,22 @@ size_t fwd_bf16_workspace_bytes(int BH, int Tq, int Tk, int d, int num_splits);
 hipError_t fwd_bf16_launch(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Tq,
                            int Tk, int d, float scale, int causal, int num_splits, void* workspace,
                            hipStream_t stream);
+// Partial state (acc, m, l) of one key range; causal blocks key j for query i
+// when j > i + diag.  m in natural-log units.
+size_t fwd_bf16_state_workspace_bytes(int BH, int Tq, int Tk, int d);
+hipError_t fwd_bf16_state_launch(const void* q, const void* k, const void* v, float* acc, float* m, float* l, int BH,
+                                 int Tq, int Tk, int d, float scale, int causal, int diag, void* workspace,
+                                 hipStream_t stream);
+// Merge of n partial states [n][BH][Tq](x d) into O (bf16) and LSE.
+hipError_t merge_states_launch(const float* acc, const float* m, const float* l, int n, void* o, float* lse, int BH,
+                               int Tq, int d, hipStream_t stream);
 
 // ---- bf16 backward --------------------------------------------------------------
 size_t bwd_bf16_workspace_bytes(int BH, int Tq, int Tk, int d);
+// dlse (may be null): upstream gradient of the loss with respect to LSE [BH][Tq].
 hipError_t bwd_bf16_launch(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                           const void* dout, void* dq, void* dk, void* dv, int BH, int Tq, int Tk, int d,
-                           float scale, int causal, void* workspace, hipStream_t stream);
+                           const float* dlse, const void* dout, void* dq, void* dk, void* dv, int BH, int Tq, int Tk,
+                           int d, float scale, int causal, void* workspace, hipStream_t stream);
 
 // ---- fp32 path (block-size faithful forward, deterministic backward) -------------
 hipError_t fwd_f32_launch(const float* q, const float* k, const float* v, float* o, float* lse, int BH, int Tq,

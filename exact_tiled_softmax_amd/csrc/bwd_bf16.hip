@@ -16,7 +16,12 @@
 // Kernels, in launch order:
 //   bwd_stats      per query row: LSE * log2(e) (+inf for a row that is
 //                  outside Tq or has no allowed key, so its P is 0) and
-//                  D = sum_c dO_c O_c, blocked 32 rows at a time
+//                  D = sum_c dO_c O_c, blocked 32 rows at a time.  With an
+//                  upstream gradient dLSE on the log-sum-exp, dS gains
+//                  dLSE_i P_ij (the row sum l is a smooth function of the
+//                  inputs that gradients flow through: "The Hidden Recurrence
+//                  in Softmax Attention", sections "Flash Attention Backward
+//                  Pass" and "Gradient at the Output"), i.e. D becomes D - dLSE.
 //   bwd_transpose  K^T ([d][Tk], Tk padded to 64 with zeros) into the
 //                  workspace, with the keys of every 16-key group in the
 //                  order the dQ MFMA operand takes them
@@ -59,8 +64,8 @@ struct BwdArgs {
 // bwd_stats: 16 lanes per query row (padded to a multiple of 32 rows per head).
 template <int D>
 __global__ __launch_bounds__(256) void bwd_stats_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ dout,
-                                                        const float* __restrict__ lse, float* __restrict__ stats,
-                                                        int BH, int Tq, int nqb32) {
+                                                        const float* __restrict__ lse, const float* __restrict__ dlse,
+                                                        float* __restrict__ stats, int BH, int Tq, int nqb32) {
   constexpr int PER = D / 16;
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   const int row = t / 16, sub = t % 16;
@@ -86,7 +91,7 @@ __global__ __launch_bounds__(256) void bwd_stats_kernel(const __bf16* __restrict
     }
     float* blk = stats + ((size_t)bh * nqb32 + qi / 32) * 64;
     blk[qi % 32] = l2;
-    blk[32 + qi % 32] = ok ? acc : 0.f;
+    blk[32 + qi % 32] = ok ? acc - (dlse ? dlse[(size_t)bh * Tq + qi] : 0.f) : 0.f;
   }
 }
 
@@ -560,14 +565,14 @@ BwdLayout bwd_layout(int BH, int Tq, int Tk, int d) {
 }
 
 template <int D>
-hipError_t bwd_launch_d(BwdArgs& args, const __bf16* o, const float* lse, bool causal, char* ws,
+hipError_t bwd_launch_d(BwdArgs& args, const __bf16* o, const float* lse, const float* dlse, bool causal, char* ws,
                         const BwdLayout& L, hipStream_t stream) {
   // pre-pass: row statistics and the transposed copy of K
   prof_begin(2, stream);
   {
     const int rows = args.BH * args.nqb32 * 32;
     hipLaunchKernelGGL(bwd_stats_kernel<D>, dim3((rows * 16 + 255) / 256), dim3(256), 0, stream, o, args.dout, lse,
-                       reinterpret_cast<float*>(ws + L.stats), args.BH, args.Tq, args.nqb32);
+                       dlse, reinterpret_cast<float*>(ws + L.stats), args.BH, args.Tq, args.nqb32);
     hipLaunchKernelGGL(transpose_rows_kernel<D>, dim3(args.Tk_pad / 64, args.BH), dim3(256), 0, stream, args.k,
                        reinterpret_cast<__bf16*>(ws + L.kt), args.Tk, args.Tk_pad);
   }
@@ -600,8 +605,8 @@ hipError_t bwd_launch_d(BwdArgs& args, const __bf16* o, const float* lse, bool c
 size_t bwd_bf16_workspace_bytes(int BH, int Tq, int Tk, int d) { return bwd_layout(BH, Tq, Tk, d).total; }
 
 hipError_t bwd_bf16_launch(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                           const void* dout, void* dq, void* dk, void* dv, int BH, int Tq, int Tk, int d,
-                           float scale, int causal, void* workspace, hipStream_t stream) {
+                           const float* dlse, const void* dout, void* dq, void* dk, void* dv, int BH, int Tq, int Tk,
+                           int d, float scale, int causal, void* workspace, hipStream_t stream) {
   const BwdLayout L = bwd_layout(BH, Tq, Tk, d);
   char* ws = static_cast<char*>(workspace);
   BwdArgs a;
@@ -622,8 +627,8 @@ hipError_t bwd_bf16_launch(const void* q, const void* k, const void* v, const vo
   a.scale = scale;
   a.scale_log2 = scale * kLog2e;
   const __bf16* ob = static_cast<const __bf16*>(o);
-  return d == 128 ? bwd_launch_d<128>(a, ob, lse, causal != 0, ws, L, stream)
-                  : bwd_launch_d<64>(a, ob, lse, causal != 0, ws, L, stream);
+  return d == 128 ? bwd_launch_d<128>(a, ob, lse, dlse, causal != 0, ws, L, stream)
+                  : bwd_launch_d<64>(a, ob, lse, dlse, causal != 0, ws, L, stream);
 }
 
 }  // namespace attn

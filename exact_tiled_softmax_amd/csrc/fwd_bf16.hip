@@ -70,9 +70,11 @@ struct FwdArgs {
   const __bf16* vt;  // V^T [BH][D][Tk_pad], keys of each 16-key group in group_row order
   __bf16* o;
   float* lse;
-  float* part_acc;  // [splits][BH][Tq][D]   (split mode)
-  float* part_ml;   // [splits][BH][Tq][2]   (split mode: m in log2 units, l)
+  float* part_acc;  // [splits][BH][Tq][D]   (split / state mode: unnormalised a)
+  float* part_m;    // [splits][BH][Tq]      (split / state mode: reference max, natural log units)
+  float* part_l;    // [splits][BH][Tq]      (split / state mode: l)
   int BH, Tq, Tk, Tk_pad;
+  int diag;          // causal: key j is blocked for query i when j > i + diag
   int num_qtiles, num_splits, keys_per_split;
   float scale_log2;  // scale * log2(e)
 };
@@ -132,7 +134,7 @@ __device__ __forceinline__ void fwd_tile(const __bf16* stg, const bf16x8 (&qf)[8
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = key0 + 32 * u + 8 * (r / 4) + 4 * hf + (r % 4);
-        s[u][r] = (key >= kend || (causal && key > row)) ? -INFINITY : s[u][r] * c;
+        s[u][r] = (key >= kend || (causal && key > row)) ? -INFINITY : s[u][r] * c;  // row: i + diag
       }
     cc = 1.f;
   }
@@ -201,11 +203,11 @@ __global__ __launch_bounds__(FwdCfg<D>::THREADS, FwdCfg<D>::WG_PER_CU) void fwd_
     kbeg = split * a.keys_per_split;
     kend = min(a.Tk, kbeg + a.keys_per_split);
   }
-  if (CAUSAL) kend = min(kend, q0 + C::BM);
+  if (CAUSAL) kend = max(kbeg, min(kend, q0 + C::BM + a.diag));
   const int ntiles = kend > kbeg ? (kend - kbeg + C::BN - 1) / C::BN : 0;
   // end of the keys this wave's rows may see (causal): whole tiles past it are
   // skipped
-  const int wave_kend = CAUSAL ? min(kend, q0 + wave * 32 + 32) : kend;
+  const int wave_kend = CAUSAL ? min(kend, q0 + wave * 32 + 32 + a.diag) : kend;
   const int wave_row0 = q0 + wave * 32;
 
   // Q fragments (B operand of S^T = K Q^T): lane holds Q[row][16*ks + 8*hf + 0..7]
@@ -238,8 +240,8 @@ __global__ __launch_bounds__(FwdCfg<D>::THREADS, FwdCfg<D>::WG_PER_CU) void fwd_
     if (t + C::AHEAD < ntiles) fwd_issue<D>(a, bh, kbeg + (t + C::AHEAD) * C::BN, stage(t + C::AHEAD), wave, lane);
     const int key0 = kbeg + t * C::BN;
     if (key0 < wave_kend) {
-      const bool need_mask = (key0 + C::BN > kend) || (CAUSAL && key0 + C::BN - 1 > wave_row0);
-      fwd_tile<D>(stage(t), qf, acc, m_ref, l_run, c, lane, need_mask, key0, kend, row, CAUSAL);
+      const bool need_mask = (key0 + C::BN > kend) || (CAUSAL && key0 + C::BN - 1 > wave_row0 + a.diag);
+      fwd_tile<D>(stage(t), qf, acc, m_ref, l_run, c, lane, need_mask, key0, kend, row + a.diag, CAUSAL);
     }
   }
 
@@ -258,8 +260,8 @@ __global__ __launch_bounds__(FwdCfg<D>::THREADS, FwdCfg<D>::WG_PER_CU) void fwd_
               f32x4{acc[cb][4 * g], acc[cb][4 * g + 1], acc[cb][4 * g + 2], acc[cb][4 * g + 3]};
         }
       if (hf == 0) {
-        a.part_ml[prow * 2 + 0] = m_ref;
-        a.part_ml[prow * 2 + 1] = l_tot;
+        a.part_m[prow] = m_ref * kLn2;  // -inf stays -inf
+        a.part_l[prow] = l_tot;
       }
     }
     return;
@@ -282,21 +284,24 @@ __global__ __launch_bounds__(FwdCfg<D>::THREADS, FwdCfg<D>::WG_PER_CU) void fwd_
   }
 }
 
-// Merge of split partial states (m_s, l_s, a_s) of one row:
-//   M = max_s m_s, l = sum_s 2^(m_s - M) l_s, a = sum_s 2^(m_s - M) a_s,
-//   O = a / l, LSE = (M + log2 l) ln 2.  One wave per row, D/64 columns per lane.
+// Merge of partial states (m_s, l_s, a_s) of one row, m in natural-log units
+// ("The Hidden Recurrence in Softmax Attention", section "Chunk-wise Mode
+// with Online Softmax Re-scale": states of key chunks combine by rescaling
+// each to the common max):
+//   M = max_s m_s, l = sum_s e^(m_s - M) l_s, a = sum_s e^(m_s - M) a_s,
+//   O = a / l, LSE = M + ln l.  One wave per row, D/64 columns per lane.
 template <int D>
 __global__ __launch_bounds__(256) void fwd_combine_kernel(const float* __restrict__ part_acc,
-                                                          const float* __restrict__ part_ml,
+                                                          const float* __restrict__ part_m,
+                                                          const float* __restrict__ part_l,
                                                           __bf16* __restrict__ o, float* __restrict__ lse,
                                                           int BH, int Tq, int num_splits) {
-  const int wave = (blockIdx.x * blockDim.x + threadIdx.x) / 64;
+  const size_t rowid = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) / 64;  // one wave per (bh, row)
   const int lane = threadIdx.x % 64;
-  if (wave >= BH * Tq) return;
-  const size_t rowid = wave;  // = bh * Tq + row
+  if (rowid >= (size_t)BH * Tq) return;
   const size_t stride = (size_t)BH * Tq;
   float M = -INFINITY;
-  for (int s = 0; s < num_splits; ++s) M = fmaxf(M, part_ml[(s * stride + rowid) * 2]);
+  for (int s = 0; s < num_splits; ++s) M = fmaxf(M, part_m[s * stride + rowid]);
   const float mu = (M == -INFINITY) ? 0.f : M;
   float l = 0.f;
   constexpr int PER = D / 64;
@@ -304,9 +309,8 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(const float* __restric
 #pragma unroll
   for (int j = 0; j < PER; ++j) acc[j] = 0.f;
   for (int s = 0; s < num_splits; ++s) {
-    const float ms = part_ml[(s * stride + rowid) * 2];
-    const float w = fast_exp2(ms - mu);
-    l += w * part_ml[(s * stride + rowid) * 2 + 1];
+    const float w = fast_exp2((part_m[s * stride + rowid] - mu) * kLog2e);  // -inf -> 0
+    l += w * part_l[s * stride + rowid];
     const float* pa = part_acc + (s * stride + rowid) * D;
 #pragma unroll
     for (int j = 0; j < PER; ++j) acc[j] += w * pa[lane + 64 * j];
@@ -314,7 +318,7 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(const float* __restric
   const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
   for (int j = 0; j < PER; ++j) o[rowid * D + lane + 64 * j] = to_bf16(acc[j] * inv);
-  if (lane == 0) lse[rowid] = l > 0.f ? (M + fast_log2(l)) * kLn2 : -INFINITY;
+  if (lane == 0) lse[rowid] = l > 0.f ? M + fast_log2(l) * kLn2 : -INFINITY;
 }
 
 template <int D, bool CAUSAL, bool SPLIT>
@@ -337,7 +341,7 @@ constexpr int kBN = 64;
 static_assert(FwdCfg<64>::BM == kBM && FwdCfg<128>::BM == kBM && FwdCfg<128>::BN == kBN, "tile sizes");
 
 struct FwdLayout {
-  size_t vt, part_acc, part_ml, total;
+  size_t vt, part_acc, part_m, part_l, total;
 };
 
 FwdLayout fwd_layout(int BH, int Tq, int Tk, int d, int num_splits) {
@@ -346,11 +350,11 @@ FwdLayout fwd_layout(int BH, int Tq, int Tk, int d, int num_splits) {
   FwdLayout L;
   L.vt = 0;
   L.part_acc = up((size_t)BH * d * tk_pad * 2);
-  L.part_ml = L.part_acc;
-  L.total = L.part_acc;
+  L.part_m = L.part_l = L.total = L.part_acc;
   if (num_splits > 1) {
-    L.part_ml = up(L.part_acc + (size_t)num_splits * BH * Tq * d * sizeof(float));
-    L.total = up(L.part_ml + (size_t)num_splits * BH * Tq * 2 * sizeof(float));
+    L.part_m = up(L.part_acc + (size_t)num_splits * BH * Tq * d * sizeof(float));
+    L.part_l = up(L.part_m + (size_t)num_splits * BH * Tq * sizeof(float));
+    L.total = up(L.part_l + (size_t)num_splits * BH * Tq * sizeof(float));
   }
   return L;
 }
@@ -379,56 +383,89 @@ size_t fwd_bf16_workspace_bytes(int BH, int Tq, int Tk, int d, int num_splits) {
   return fwd_layout(BH, Tq, Tk, d, num_splits).total;
 }
 
-hipError_t fwd_bf16_launch(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Tq,
-                           int Tk, int d, float scale, int causal, int num_splits, void* workspace,
-                           hipStream_t stream) {
-  const FwdLayout L = fwd_layout(BH, Tq, Tk, d, num_splits);
-  char* ws = static_cast<char*>(workspace);
+namespace {
+
+FwdArgs fwd_args(const void* q, const void* k, void* o, float* lse, int BH, int Tq, int Tk, float scale,
+                 int num_splits, int diag, const void* vt) {
   FwdArgs args;
   args.q = static_cast<const __bf16*>(q);
   args.k = static_cast<const __bf16*>(k);
-  args.vt = reinterpret_cast<const __bf16*>(ws + L.vt);
+  args.vt = static_cast<const __bf16*>(vt);
   args.o = static_cast<__bf16*>(o);
   args.lse = lse;
+  args.part_acc = args.part_m = args.part_l = nullptr;
   args.BH = BH;
   args.Tq = Tq;
   args.Tk = Tk;
   args.Tk_pad = (Tk + kBN - 1) / kBN * kBN;
+  args.diag = diag;
   args.num_qtiles = (Tq + kBM - 1) / kBM;
   args.num_splits = num_splits;
   const int kblocks = (Tk + kBN - 1) / kBN;
   args.keys_per_split = ((kblocks + num_splits - 1) / num_splits) * kBN;
   args.scale_log2 = scale * kLog2e;
-  const bool split = num_splits > 1;
-  args.part_acc = split ? reinterpret_cast<float*>(ws + L.part_acc) : nullptr;
-  args.part_ml = split ? reinterpret_cast<float*>(ws + L.part_ml) : nullptr;
+  return args;
+}
 
-  // V^T for the A operand of a += V^T P^T
+// V^T copy (profiled as the forward's auxiliary work), then the main kernel.
+hipError_t fwd_run(const FwdArgs& args, const void* v, void* vt, int d, bool causal, bool split, hipStream_t stream) {
   prof_begin(1, stream);
   if (d == 128)
-    hipLaunchKernelGGL(transpose_rows_kernel<128>, dim3(args.Tk_pad / 64, BH), dim3(256), 0, stream,
-                       static_cast<const __bf16*>(v), reinterpret_cast<__bf16*>(ws + L.vt), Tk, args.Tk_pad);
+    hipLaunchKernelGGL(transpose_rows_kernel<128>, dim3(args.Tk_pad / 64, args.BH), dim3(256), 0, stream,
+                       static_cast<const __bf16*>(v), static_cast<__bf16*>(vt), args.Tk, args.Tk_pad);
   else
-    hipLaunchKernelGGL(transpose_rows_kernel<64>, dim3(args.Tk_pad / 64, BH), dim3(256), 0, stream,
-                       static_cast<const __bf16*>(v), reinterpret_cast<__bf16*>(ws + L.vt), Tk, args.Tk_pad);
+    hipLaunchKernelGGL(transpose_rows_kernel<64>, dim3(args.Tk_pad / 64, args.BH), dim3(256), 0, stream,
+                       static_cast<const __bf16*>(v), static_cast<__bf16*>(vt), args.Tk, args.Tk_pad);
   prof_end(1, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  return (d == 128) ? fwd_dispatch<128>(args, causal, split, stream) : fwd_dispatch<64>(args, causal, split, stream);
+}
 
-  e = (d == 128) ? fwd_dispatch<128>(args, causal != 0, split, stream)
-                 : fwd_dispatch<64>(args, causal != 0, split, stream);
-  if (e != hipSuccess || !split) return e;
-  const int rows = BH * Tq;
-  const int blocks = (rows + 3) / 4;
+}  // namespace
+
+hipError_t merge_states_launch(const float* acc, const float* m, const float* l, int n, void* o, float* lse, int BH,
+                               int Tq, int d, hipStream_t stream) {
+  const unsigned blocks = (unsigned)(((size_t)BH * Tq + 3) / 4);
   prof_begin(1, stream);
   if (d == 128)
-    hipLaunchKernelGGL(fwd_combine_kernel<128>, dim3(blocks), dim3(256), 0, stream, args.part_acc, args.part_ml,
-                       args.o, lse, BH, Tq, num_splits);
+    hipLaunchKernelGGL(fwd_combine_kernel<128>, dim3(blocks), dim3(256), 0, stream, acc, m, l,
+                       static_cast<__bf16*>(o), lse, BH, Tq, n);
   else
-    hipLaunchKernelGGL(fwd_combine_kernel<64>, dim3(blocks), dim3(256), 0, stream, args.part_acc, args.part_ml,
-                       args.o, lse, BH, Tq, num_splits);
+    hipLaunchKernelGGL(fwd_combine_kernel<64>, dim3(blocks), dim3(256), 0, stream, acc, m, l,
+                       static_cast<__bf16*>(o), lse, BH, Tq, n);
   prof_end(1, stream);
   return hipGetLastError();
+}
+
+hipError_t fwd_bf16_launch(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Tq,
+                           int Tk, int d, float scale, int causal, int num_splits, void* workspace,
+                           hipStream_t stream) {
+  const FwdLayout L = fwd_layout(BH, Tq, Tk, d, num_splits);
+  char* ws = static_cast<char*>(workspace);
+  FwdArgs args = fwd_args(q, k, o, lse, BH, Tq, Tk, scale, num_splits, 0, ws + L.vt);
+  const bool split = num_splits > 1;
+  if (split) {
+    args.part_acc = reinterpret_cast<float*>(ws + L.part_acc);
+    args.part_m = reinterpret_cast<float*>(ws + L.part_m);
+    args.part_l = reinterpret_cast<float*>(ws + L.part_l);
+  }
+  hipError_t e = fwd_run(args, v, ws + L.vt, d, causal != 0, split, stream);
+  if (e != hipSuccess || !split) return e;
+  return merge_states_launch(args.part_acc, args.part_m, args.part_l, num_splits, o, lse, BH, Tq, d, stream);
+}
+
+size_t fwd_bf16_state_workspace_bytes(int BH, int Tq, int Tk, int d) { return fwd_layout(BH, Tq, Tk, d, 1).total; }
+
+hipError_t fwd_bf16_state_launch(const void* q, const void* k, const void* v, float* acc, float* m, float* l, int BH,
+                                 int Tq, int Tk, int d, float scale, int causal, int diag, void* workspace,
+                                 hipStream_t stream) {
+  char* ws = static_cast<char*>(workspace);
+  FwdArgs args = fwd_args(q, k, nullptr, nullptr, BH, Tq, Tk, scale, 1, diag, ws);
+  args.part_acc = acc;
+  args.part_m = m;
+  args.part_l = l;
+  return fwd_run(args, v, ws, d, causal != 0, true, stream);
 }
 
 }  // namespace attn

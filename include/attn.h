@@ -123,6 +123,66 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
              void* stream);
 
 /*
+ * attn_bwd_dlse - attn_bwd with an upstream gradient on the LSE output.
+ *   dlse : fp32 [B,H,Tq], d(loss)/d(LSE_i) (required; NULL is
+ *          ATTN_ERR_INVALID_ARG).  Other arguments as attn_bwd.
+ * LSE_i = m_i + log l_i, and gradients flow through the row sum l ("The
+ * Hidden Recurrence in Softmax Attention", sections "Flash Attention Backward
+ * Pass" and "Gradient at the Output"); with d LSE_i / d S_ij = P_ij the
+ * gradient of the scores becomes dS = P o (dP - D + dlse): D_i is replaced by
+ * D_i - dlse_i.
+ * This lets a caller that merged key-range states (attn_merge_states)
+ * propagate a gradient through the merged LSE.
+ */
+int attn_bwd_dlse(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                  const float* dlse, const void* dout, void* dq, void* dk, void* dv_grad,
+                  int B, int H, int Tq, int Tk, int d, int dv, float scale, int causal,
+                  void* stream);
+
+/*
+ * attn_fwd_state - the unnormalised online-softmax state of one key range
+ * ("Tiled attention with an online softmax", section "Task": a row's state is
+ * its running max m, running sum l and accumulator a; "The Hidden Recurrence
+ * in Softmax Attention", section "Chunk-wise Mode with Online Softmax
+ * Re-scale": states of separate key chunks combine by rescaling to a common
+ * max, see attn_merge_states).
+ *   q [B,H,Tq,d], k [B,H,Tk,d], v [B,H,Tk,dv] : bf16, this call's queries and
+ *             this key range (layout as above).
+ *   acc       : fp32 output [B,H,Tq,dv], a_i = sum_j exp(s_ij - m_i) v_j over
+ *               the allowed keys j (exp(s - m) rounded to bf16 in the product
+ *               with v, as in attn_fwd).
+ *   m         : fp32 output [B,H,Tq], natural-log units: a reference value at
+ *               most 8 ln 2 (about 5.55) below the largest allowed scaled
+ *               score s_ij = scale q_i.k_j of row i and not above it (the
+ *               library moves its reference lazily); -inf if row i has no
+ *               allowed key in this range.
+ *   l         : fp32 output [B,H,Tq], l_i = sum_j exp(s_ij - m_i) (0 if none).
+ *   a_i / l_i and m_i + ln l_i do not depend on which reference m_i is used.
+ *   q_offset, k_offset : >= 0, global positions of this call's first query and
+ *               first key; with causal != 0, key j is blocked for query i when
+ *               k_offset + j > q_offset + i (the top-left rule of attn_fwd on
+ *               global indices).  Ignored when causal == 0.
+ * Supported: d == dv, d in {64, 128}.  Workspace: a transposed copy of v.
+ */
+int attn_fwd_state(const void* q, const void* k, const void* v, float* acc, float* m, float* l,
+                   int B, int H, int Tq, int Tk, int d, int dv, float scale, int causal,
+                   int q_offset, int k_offset, void* stream);
+
+/*
+ * attn_merge_states - O and LSE from n partial states of the same queries
+ * (the rescale rule of "The Hidden Recurrence in Softmax Attention", section
+ * "Chunk-wise Mode with Online Softmax Re-scale"):
+ *   M = max_s m_s,  l = sum_s exp(m_s - M) l_s,  a = sum_s exp(m_s - M) a_s,
+ *   O = a / l (bf16, 0 where l = 0),  LSE = M + ln l (-inf where l = 0).
+ *   acc [n,B,H,Tq,dv], m [n,B,H,Tq], l [n,B,H,Tq] : fp32 inputs, state s at
+ *               index s (as written by attn_fwd_state).
+ *   o [B,H,Tq,dv] bf16 and lse [B,H,Tq] fp32 : outputs.
+ *   n >= 1; dv in {64, 128} (else ATTN_ERR_UNSUPPORTED).
+ */
+int attn_merge_states(const float* acc, const float* m, const float* l, int n, void* o, float* lse,
+                      int B, int H, int Tq, int dv, void* stream);
+
+/*
  * attn_fwd_f32 - fp32 forward that follows the page's block loop literally:
  * keys are taken in blocks of `block_n` starting at 0, block_n, 2*block_n, ...
  * (the last may be shorter) and each block updates (m, l, a) with one online

@@ -80,6 +80,47 @@ def test_bwd_invalid_and_unsupported(lib):
     assert lib.attn_bwd(*a) == attn.ATTN_ERR_INVALID_ARG
 
 
+def test_bwd_dlse_validates(lib):
+    args = [NZ] * 10 + [1, 1, 8, 8, 64, 64, 0.125, 1, None]
+    for i in range(10):  # every pointer, dlse (index 5) included, is required
+        a = list(args)
+        a[i] = None
+        assert lib.attn_bwd_dlse(*a) == attn.ATTN_ERR_INVALID_ARG
+    a = list(args)
+    a[14] = a[15] = 96
+    assert lib.attn_bwd_dlse(*a) == attn.ATTN_ERR_UNSUPPORTED
+
+
+def test_fwd_state_validates(lib):
+    args = [NZ] * 6 + [1, 1, 8, 8, 64, 64, 0.125, 1, 0, 0, None]
+    for i in range(6):
+        a = list(args)
+        a[i] = None
+        assert lib.attn_fwd_state(*a) == attn.ATTN_ERR_INVALID_ARG
+    for i, bad in ((6, 0), (8, 0), (12, -0.5), (14, -1), (15, -3)):  # B, Tq, scale, q_offset, k_offset
+        a = list(args)
+        a[i] = bad
+        assert lib.attn_fwd_state(*a) == attn.ATTN_ERR_INVALID_ARG
+    a = list(args)
+    a[10] = a[11] = 80
+    assert lib.attn_fwd_state(*a) == attn.ATTN_ERR_UNSUPPORTED
+
+
+def test_merge_states_validates(lib):
+    args = [NZ, NZ, NZ, 2, NZ, NZ, 1, 1, 8, 64, None]
+    for i in (0, 1, 2, 4, 5):
+        a = list(args)
+        a[i] = None
+        assert lib.attn_merge_states(*a) == attn.ATTN_ERR_INVALID_ARG
+    for i, bad in ((3, 0), (6, 0), (8, -1), (9, 0)):
+        a = list(args)
+        a[i] = bad
+        assert lib.attn_merge_states(*a) == attn.ATTN_ERR_INVALID_ARG
+    a = list(args)
+    a[9] = 96
+    assert lib.attn_merge_states(*a) == attn.ATTN_ERR_UNSUPPORTED
+
+
 def test_f32_entry_points_validate(lib):
     base = [NZ] * 5 + [1, 1, 8, 8, 64, 64, 0.125, 0]
     assert lib.attn_fwd_f32(*base, -1, None) == attn.ATTN_ERR_INVALID_ARG
