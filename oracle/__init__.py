@@ -7,6 +7,7 @@ from .attention_oracle import (  # noqa: F401
     backward_dq_rows,
     causal_blocked,
     dense_backward,
+    decode_forward,
     dense_forward,
     forward_rows,
     merge_states,

@@ -38,6 +38,10 @@ full score rows materialised:
   "The Hidden Recurrence in Softmax Attention", section "Chunk-wise Mode with
   Online Softmax Re-scale" (each state rescaled by exp(m_s - max), summed;
   O = a / l, LSE = max + ln l).
+* Decode.  The newest Tq queries of each sequence against the first L_b
+  slots of a key cache, query i at position L_b - Tq + i ("The Hidden
+  Recurrence in Softmax Attention", section "Recurrent mode": the query of
+  step t sees the keys of steps up to t); the plain definition per row.
 * Gradient of the log-sum-exp.  When a caller also differentiates LSE, its
   upstream gradient dLSE adds dLSE o P to dS, since d LSE_i / d S_ij = P_ij
   ("Flash Attention Backward Pass", which treats l as a smooth function of the
@@ -212,6 +216,40 @@ def merge_states(ms, ls, accs):
     with np.errstate(divide="ignore", invalid="ignore"):
         o = np.where(l[..., None] > 0, acc / np.where(l > 0, l, 1.0)[..., None], 0.0)
         lse = np.where(l > 0, mu + np.log(np.where(l > 0, l, 1.0)), NEG_INF)
+    return o, lse
+
+
+# --- Decode: a few newest queries against a cache of keys --------------------
+
+def decode_forward(q, k, v, scale, kv_lens=None, causal=False):
+    """Attention of the newest queries of each sequence over its cached keys
+    (the recurrent mode of "The Hidden Recurrence in Softmax Attention",
+    section "Recurrent mode": the query at step t sees the keys of steps up
+    to t).
+
+    q [B, H, Tq, d]; k [B, H, Tk, d], v [B, H, Tk, dv] hold Tk cache slots;
+    sequence b uses the first L_b = clip(kv_lens[b], 0, Tk) of them (all Tk
+    when kv_lens is None).  Query i of sequence b sits at position
+    L_b - Tq + i.  With `causal`, key j is blocked for it when
+    j > L_b - Tq + i; otherwise every cached key j < L_b is allowed.  A query
+    with no allowed key gets O = 0 and LSE = -inf.  Returns (o [B, H, Tq, dv],
+    lse [B, H, Tq]), each row from its complete score row."""
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    B, H, tq, _ = q.shape
+    tk = k.shape[2]
+    lens = np.full(B, tk) if kv_lens is None else np.clip(np.asarray(kv_lens, dtype=np.int64), 0, tk)
+    o = np.zeros((B, H, tq, v.shape[3]))
+    lse = np.full((B, H, tq), NEG_INF)
+    for b in range(B):
+        n = int(lens[b])
+        if n == 0:
+            continue
+        for h in range(H):
+            s = scale * (q[b, h] @ k[b, h, :n].T)
+            if causal:
+                s = np.where(causal_blocked(tq, n, row0=n - tq), NEG_INF, s)
+            p, lse[b, h] = _softmax_rows(s)
+            o[b, h] = p @ v[b, h, :n]
     return o, lse
 
 

@@ -8,6 +8,8 @@ import json
 import os
 import types
 
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -215,6 +217,55 @@ def pin_state_merge(mod):
                 and np.allclose(a1, a2, rtol=1e-13, atol=1e-14)):
             return False
     return True
+
+
+def _recurrent_mode(q_row, k, v, scale, last):
+    """The page's recurrent mode for one query, token by token over the keys of
+    steps 0..last, without any rescale: l_t = l_{t-1} + exp(s_t),
+    a_t = a_{t-1} + exp(s_t) v_t; the output is a/l, LSE = ln l (valid while the
+    scores stay small)."""
+    l, a = 0.0, np.zeros(v.shape[1])
+    for t in range(last + 1):
+        e = math.exp(scale * float(q_row @ k[t]))
+        l, a = l + e, a + e * v[t]
+    return (a / l, math.log(l)) if l > 0 else (np.zeros(v.shape[1]), -math.inf)
+
+
+def pin_decode(mod):
+    """Decode against the page's un-rescaled recurrent mode (small scores), the
+    dense forward when Tq = Tk, cache slots past each length poisoned with NaN,
+    and the empty cases."""
+    r = _rng(61)
+    B, H, tq, tk, d, dv = 3, 2, 3, 9, 4, 3
+    q = r.standard_normal((B, H, tq, d))
+    k = r.standard_normal((B, H, tk, d))
+    v = r.standard_normal((B, H, tk, dv))
+    lens = np.array([9, 5, 2])
+    kp, vp = k.copy(), v.copy()
+    for b, n in enumerate(lens):
+        kp[b, :, n:] = np.nan
+        vp[b, :, n:] = np.nan
+    for causal in (False, True):
+        o, lse = mod.decode_forward(q, kp, vp, 0.4, kv_lens=lens, causal=causal)
+        for b in range(B):
+            for h in range(H):
+                for i in range(tq):
+                    last = lens[b] - tq + i if causal else lens[b] - 1
+                    ro, rl = _recurrent_mode(q[b, h, i], k[b, h], v[b, h], 0.4, last)
+                    if not (np.allclose(o[b, h, i], ro, rtol=1e-12, atol=1e-13) and
+                            (rl == lse[b, h, i] or abs(rl - lse[b, h, i]) < 1e-12)):
+                        return False
+    # Tq = Tk = every length: the newest-queries rule is the top-left rule
+    qf = r.standard_normal((2, 2, 7, d))
+    kf, vf = r.standard_normal((2, 2, 7, d)), r.standard_normal((2, 2, 7, dv))
+    for causal in (False, True):
+        o, lse = mod.decode_forward(qf, kf, vf, 0.8, causal=causal)
+        ro, rl = mod.dense_forward(qf, kf, vf, 0.8, causal)
+        if not (np.allclose(o, ro, atol=1e-13) and np.allclose(lse, rl, atol=1e-13)):
+            return False
+    o, lse = mod.decode_forward(q, k, v, 0.4, kv_lens=[0, 9, 1], causal=True)
+    return bool(np.all(o[0] == 0) and np.all(np.isneginf(lse[0])) and np.all(np.isneginf(lse[2, :, :2]))
+                and np.all(np.isfinite(lse[2, :, 2])) and np.allclose(o[2, :, 2], v[2, :, 0]))
 
 
 def pin_block_invariance(mod):
@@ -461,6 +512,8 @@ MUTANTS = {
                               "causal_blocked(s.shape[-2], s.shape[-1])"),
     "merge_weight_inverted": ("w = np.exp(m_s - mu)", "w = np.exp(mu - m_s)"),
     "merge_l_unweighted": ("l = l + w * _as_f64(l_s)", "l = l + _as_f64(l_s)"),
+    "decode_query_position_off_by_one": ("causal_blocked(tq, n, row0=n - tq)", "causal_blocked(tq, n, row0=n - tq + 1)"),
+    "decode_values_misindexed": ("o[b, h] = p @ v[b, h, :n]", "o[b, h] = p @ v[b, h, :n][::-1]"),
 }
 
 
@@ -486,6 +539,7 @@ def _all_pins_pass(mod, g):
         lambda: pin_state_merge(mod),
         lambda: pin_torch_dlse(mod),
         lambda: pin_fd_dlse(mod),
+        lambda: pin_decode(mod),
     ]
     for c in checks:
         try:
@@ -500,6 +554,10 @@ def _all_pins_pass(mod, g):
 def test_dlse_backward_matches_finite_differences_and_torch():
     assert pin_fd_dlse(ao)
     assert pin_torch_dlse(ao)
+
+
+def test_decode_matches_recurrent_mode_and_dense_forward():
+    assert pin_decode(ao)
 
 
 def test_merged_key_range_states_equal_dense_forward():
