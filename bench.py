@@ -16,6 +16,11 @@ Throughput counts algorithmic flops only: with `pairs` the number of unmasked
 Prints one JSON line.  Also reports the dominant kernel against its roofline
 (HIP-event durations recorded by the library on the launch stream) and the
 float64 CPU oracle timed on a bounded sample of the same workload.
+
+--workload decode_bf16_b8h32_tk32768_d128 times attn_decode instead (one new
+query per sequence against a key/value cache of mixed lengths): the metric is
+then HBM GB/s of the algorithmic bytes (every cached key and value row read
+once, q read, o and lse written) against the 8 TB/s HBM peak.
 """
 from __future__ import annotations
 
@@ -78,10 +83,11 @@ def kernel_source_digest(files):
     return h.hexdigest()[:16]
 
 
-KERNEL_SOURCES = {"fwd": ["fwd_bf16.hip", "attn_common.hpp", "tile_stream.hpp"],
+KERNEL_SOURCES = {"decode": ["decode_bf16.hip", "attn_common.hpp"],
+                  "fwd": ["fwd_bf16.hip", "attn_common.hpp", "tile_stream.hpp"],
                   "bwd_dkdv": ["bwd_bf16.hip", "attn_common.hpp", "tile_stream.hpp"],
                   "bwd_dq": ["bwd_bf16.hip", "attn_common.hpp", "tile_stream.hpp"]}
-KERNEL_SYMBOL = {"fwd": "fwd_bf16_kernel", "bwd_dkdv": "bwd_dkdv_kernel", "bwd_dq": "bwd_dq_kernel"}
+KERNEL_SYMBOL = {"decode": "decode_bf16_kernel", "fwd": "fwd_bf16_kernel", "bwd_dkdv": "bwd_dkdv_kernel", "bwd_dq": "bwd_dq_kernel"}
 
 
 def measured_traffic(kernel: str, workload: str):
@@ -137,6 +143,128 @@ def cpu_baseline(w, budget_s: float):
     }
 
 
+def decode_bytes(w, lens):
+    """Algorithmic HBM bytes of one decode call: each sequence's cached key and
+    value rows (bf16) read once, q read, o (bf16) and lse (fp32) written."""
+    e = 2
+    kv = int(sum(int(n) for n in lens)) * w.H * e * (w.d + w.dv)
+    return kv + w.B * w.H * w.Tq * (e * w.d + e * w.dv + 4)
+
+
+def cpu_baseline_decode(w, lens, budget_s: float):
+    """The float64 oracle decode on whole sequences of the workload (all heads
+    of a sequence), as many sequences as fit in about `budget_s` seconds."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from exact_tiled_softmax_amd.inputs import make_head
+    from oracle import decode_forward
+
+    done, nbytes, elapsed = [], 0, 0.0
+    for b in range(w.B):
+        n = int(lens[b])
+        q = np.stack([make_head(w, "q", b, h) for h in range(w.H)])[None]
+        k = np.stack([make_head(w, "k", b, h)[:n] for h in range(w.H)])[None]
+        v = np.stack([make_head(w, "v", b, h)[:n] for h in range(w.H)])[None]
+        t0 = time.perf_counter()
+        o, lse = decode_forward(q, k, v, w.scale, kv_lens=[n], causal=w.causal)
+        elapsed += time.perf_counter() - t0
+        assert np.isfinite(o).all()
+        done.append(b)
+        nbytes += w.H * n * 2 * (w.d + w.dv) + w.H * w.Tq * (2 * w.d + 2 * w.dv + 4)
+        if elapsed >= budget_s:
+            break
+    threads = 1
+    for info in threadpool_info():
+        if info.get("user_api") == "blas":
+            threads = max(threads, int(info.get("num_threads", 1)))
+    return {
+        "value": nbytes / elapsed / 1e9,
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{len(done)} of {w.B} sequences of {w.name} (all {w.H} heads each, cache lengths "
+                   f"{[int(lens[b]) for b in done]}), float64 numpy, {elapsed:.1f} s; same algorithmic byte count "
+                   f"as the GPU"),
+    }
+
+
+def bench_decode(args, w) -> int:
+    import torch
+
+    from exact_tiled_softmax_amd import attn
+    from exact_tiled_softmax_amd.inputs import kv_lens, make_tensor
+
+    dev = torch.device("cuda:0")
+    lens_np = kv_lens(w)
+    print(f"[bench] building inputs for {w.name}", file=sys.stderr, flush=True)
+    q, k, v = (make_tensor(w, n).to(dev) for n in ("q", "k", "v"))
+    lens = torch.from_numpy(lens_np).to(dev)
+    o = torch.empty((w.B, w.H, w.Tq, w.dv), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.H, w.Tq), dtype=torch.float32, device=dev)
+
+    def step():
+        attn.decode(q, k, v, kv_lens=lens, scale=w.scale, causal=w.causal, out=o, lse=lse,
+                    num_splits=args.decode_splits or None)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
+    attn.profile_start()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    attn.profile_stop()
+    kern = {name: attn.profile_query(kind) for kind, name in attn.KERNEL_NAMES.items()}
+
+    nbytes = decode_bytes(w, lens_np)
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    gbs = nbytes / (ms_step * 1e-3) / 1e9
+    dom_ms = kern["decode"][0] / max(1, kern["decode"][1])
+    achieved = nbytes / (dom_ms * 1e-3) / 1e9
+    roofline = {
+        "kernel": KERNEL_SYMBOL["decode"],
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": PEAK_HBM_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / PEAK_HBM_GBS, 4),
+        "traffic": measured_traffic("decode", w.name),
+        "avg_launch_ms": round(dom_ms, 4),
+        "launches": kern["decode"][1],
+        "algorithmic_bytes_per_launch": nbytes,
+    }
+    cpu = None
+    if args.cpu_budget > 0:
+        print(f"[bench] timing the CPU oracle (~{args.cpu_budget:.0f} s)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline_decode(w, lens_np, args.cpu_budget)
+    line = {
+        "metric": "decode HBM GB/s (algorithmic bytes), bf16 d=128, 1 query against a mixed-length KV cache",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Tq": w.Tq, "Tk": w.Tk, "d": w.d, "dv": w.dv,
+                   "causal": w.causal, "kv_lens": [int(x) for x in lens_np], "step": "attn_decode"},
+        "kernel_ms_per_step": {n: round(kern[n][0] / args.steps, 4) for n in kern if kern[n][1]},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -147,6 +275,8 @@ def main(argv=None) -> int:
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the reference kernel "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes) and exit")
+    ap.add_argument("--decode-splits", type=int, default=0,
+                    help="decode workloads: key-range splits per sequence (0 = the library's choice)")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -175,6 +305,8 @@ def main(argv=None) -> int:
     if w.dtype != "bf16":
         print("bench.py times the bf16 path", file=sys.stderr)
         return 2
+    if w.decode:
+        return bench_decode(args, w)
     dev = torch.device("cuda:0")
     print(f"[bench] building inputs for {w.name}", file=sys.stderr, flush=True)
     q, k, v, do = (make_tensor(w, n).to(dev) for n in ("q", "k", "v", "do"))

@@ -22,7 +22,7 @@ ATTN_ERR_UNSUPPORTED = -2
 ATTN_ERR_HIP = -3
 
 EXPORTED = ("attn_fwd", "attn_fwd_splits", "attn_bwd", "attn_bwd_dlse", "attn_fwd_state", "attn_merge_states",
-            "attn_fwd_f32", "attn_bwd_f32", "attn_strerror", "attn_last_hip_error", "attn_profile_start",
+            "attn_decode", "attn_decode_splits", "attn_fwd_f32", "attn_bwd_f32", "attn_strerror", "attn_last_hip_error", "attn_profile_start",
             "attn_profile_stop", "attn_profile_query")
 
 # kernel kinds of attn_profile_query (include/attn.h)
@@ -31,7 +31,9 @@ KERNEL_FWD_AUX = 1
 KERNEL_BWD_PREP = 2
 KERNEL_BWD_DKDV = 3
 KERNEL_BWD_DQ = 4
-KERNEL_NAMES = {0: "fwd", 1: "fwd_aux", 2: "bwd_prep", 3: "bwd_dkdv", 4: "bwd_dq"}
+KERNEL_DECODE = 5
+KERNEL_NAMES = {0: "fwd", 1: "fwd_aux", 2: "bwd_prep", 3: "bwd_dkdv", 4: "bwd_dq", 5: "decode"}
+DECODE_MAX_QUERIES = 4
 
 _lib = None
 
@@ -58,10 +60,12 @@ def load() -> ctypes.CDLL:
     lib.attn_bwd_dlse.argtypes = [P, P, P, P, P, P, P, P, P, P, *dims, P]
     lib.attn_fwd_state.argtypes = [P, P, P, P, P, P, *dims, I, I, P]
     lib.attn_merge_states.argtypes = [P, P, P, I, P, P, I, I, I, I, P]
+    lib.attn_decode.argtypes = [P, P, P, P, P, P, *dims, P]
+    lib.attn_decode_splits.argtypes = [P, P, P, P, P, P, *dims, I, P]
     lib.attn_fwd_f32.argtypes = [P, P, P, P, P, *dims, I, P]
     lib.attn_bwd_f32.argtypes = [P, P, P, P, P, P, P, P, P, *dims, P]
     for fn in ("attn_fwd", "attn_fwd_splits", "attn_bwd", "attn_bwd_dlse", "attn_fwd_state", "attn_merge_states",
-               "attn_fwd_f32", "attn_bwd_f32"):
+               "attn_decode", "attn_decode_splits", "attn_fwd_f32", "attn_bwd_f32"):
         getattr(lib, fn).restype = I
     lib.attn_strerror.argtypes = [I]
     lib.attn_strerror.restype = ctypes.c_char_p
@@ -198,6 +202,38 @@ def merge_states(acc, m, l):
     rc = lib.attn_merge_states(_ptr(acc), _ptr(m), _ptr(l), n, _ptr(o), _ptr(lse), B, H, Tq, dv, _stream(dev))
     _check("attn_merge_states", rc)
     return o, lse
+
+
+def decode(q, k, v, kv_lens=None, scale=None, causal=False, out=None, lse=None, num_splits=None):
+    """bf16 decode: the Tq (<= 4) newest queries q [B,H,Tq,d] of each sequence
+    against the key/value cache k, v [B,H,Tk,d]; kv_lens (int32 [B] on the
+    device, optional) gives each sequence's cache length.  Returns
+    (o [B,H,Tq,dv] bf16, lse [B,H,Tq] fp32)."""
+    lib = load()
+    B, H, Tq, Tk, d, dv = _dims(q, k, v)
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, torch.bfloat16, dev)
+    if kv_lens is not None:
+        _need(kv_lens, "kv_lens", torch.int32, dev)
+        if kv_lens.shape != (B,):
+            raise ValueError(f"kv_lens must have shape ({B},), got {tuple(kv_lens.shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, Tq, dv), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H, Tq), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.bfloat16, dev)
+    _need(lse, "lse", torch.float32, dev)
+    lens = 0 if kv_lens is None else _ptr(kv_lens)
+    args = (_ptr(q), _ptr(k), _ptr(v), lens, _ptr(out), _ptr(lse), B, H, Tq, Tk, d, dv, float(scale),
+            int(bool(causal)))
+    if num_splits is None:
+        _check("attn_decode", lib.attn_decode(*args, _stream(dev)))
+    else:
+        _check("attn_decode_splits", lib.attn_decode_splits(*args, int(num_splits), _stream(dev)))
+    return out, lse
 
 
 def fwd_f32(q, k, v, scale=None, causal=False, block_n=0, out=None, lse=None):

@@ -86,6 +86,29 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
 }
 
+int decode_impl(const void* q, const void* k, const void* v, const int* kv_lens, void* o, float* lse, int B, int H,
+                int Tq, int Tk, int d, int dv, float scale, int causal, int num_splits, void* stream) {
+  int rc = check_common(q, k, v, o, lse, B, H, Tq, Tk, d, dv, scale);
+  if (rc != ATTN_OK) return rc;
+  if (num_splits < 0) return ATTN_ERR_INVALID_ARG;
+  if (!bf16_dims_supported(d, dv) || Tq > ATTN_DECODE_MAX_QUERIES) return ATTN_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int BH = B * H;
+  const int splits = attn::decode_bf16_num_splits(BH, Tk, d, num_splits);
+  const size_t ws_bytes = attn::decode_bf16_workspace_bytes(BH, Tq, d, splits);
+  void* ws = nullptr;
+  if (ws_bytes) {
+    hipError_t e = hipMallocAsync(&ws, ws_bytes, s);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  hipError_t e = attn::decode_bf16_launch(q, k, v, kv_lens, o, lse, B, H, Tq, Tk, d, scale, causal, splits, ws, s);
+  if (ws) {
+    hipError_t f = hipFreeAsync(ws, s);
+    if (e == hipSuccess) e = f;
+  }
+  return e == hipSuccess ? ATTN_OK : hip_fail(e);
+}
+
 // ---- event profiler ----------------------------------------------------------
 struct Prof {
   std::mutex mu;
@@ -242,6 +265,16 @@ int attn_merge_states(const float* acc, const float* m, const float* l, int n, v
   if (dv != 64 && dv != 128) return ATTN_ERR_UNSUPPORTED;
   hipError_t e = attn::merge_states_launch(acc, m, l, n, o, lse, B * H, Tq, dv, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
+}
+
+int attn_decode(const void* q, const void* k, const void* v, const int* kv_lens, void* o, float* lse, int B, int H,
+                int Tq, int Tk, int d, int dv, float scale, int causal, void* stream) {
+  return decode_impl(q, k, v, kv_lens, o, lse, B, H, Tq, Tk, d, dv, scale, causal, 0, stream);
+}
+
+int attn_decode_splits(const void* q, const void* k, const void* v, const int* kv_lens, void* o, float* lse, int B,
+                       int H, int Tq, int Tk, int d, int dv, float scale, int causal, int num_splits, void* stream) {
+  return decode_impl(q, k, v, kv_lens, o, lse, B, H, Tq, Tk, d, dv, scale, causal, num_splits, stream);
 }
 
 int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int Tq, int Tk,

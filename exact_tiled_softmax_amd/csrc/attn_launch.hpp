@@ -38,6 +38,15 @@ hipError_t bwd_bf16_launch(const void* q, const void* k, const void* v, const vo
                            const float* dlse, const void* dout, void* dq, void* dk, void* dv, int BH, int Tq, int Tk,
                            int d, float scale, int causal, void* workspace, hipStream_t stream);
 
+// ---- bf16 decode (newest 1..4 queries against a key cache) -----------------------
+int decode_bf16_num_splits(int BH, int Tk, int d, int requested);
+size_t decode_bf16_workspace_bytes(int BH, int Tq, int d, int num_splits);
+// kv_lens: device int32 [B] or null; query i of sequence b sits at position
+// len_b - Tq + i.
+hipError_t decode_bf16_launch(const void* q, const void* k, const void* v, const int* kv_lens, void* o, float* lse,
+                              int B, int H, int Tq, int Tk, int d, float scale, int causal, int num_splits,
+                              void* workspace, hipStream_t stream);
+
 // ---- fp32 path (block-size faithful forward, deterministic backward) -------------
 hipError_t fwd_f32_launch(const float* q, const float* k, const float* v, float* o, float* lse, int BH, int Tq,
                           int Tk, int d, int dv, float scale, int causal, int block_n, hipStream_t stream);

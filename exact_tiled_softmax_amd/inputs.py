@@ -33,6 +33,9 @@ class Workload:
     causal: bool
     dtype: str  # "bf16" or "f32"
     sigma: dict = field(default_factory=dict)  # per-tensor std, default 1
+    # decode workloads: Tq newest queries against Tk cache slots, sequence b
+    # using the first kv_lens(w)[b] of them
+    decode: bool = False
 
     @property
     def scale(self) -> float:
@@ -62,8 +65,20 @@ WORKLOADS = {
         Workload("bwd_causal_bf16_b2h16_t4096_d128", 4, 2, 16, 4096, 4096, 128, 128, True, "bf16"),
         Workload("longkv_bf16_b1h64_tq256_tk65536_d128", 5, 1, 64, 256, 65536, 128, 128, False, "bf16",
                  sigma={"q": 2.0}),
+        # decode: one new query per sequence against a 32768-slot cache, 8
+        # sequences of mixed lengths (kv_lens), 32 heads
+        Workload("decode_bf16_b8h32_tk32768_d128", 6, 8, 32, 1, 32768, 128, 128, True, "bf16", decode=True),
     ]
 }
+
+
+def kv_lens(w: Workload) -> np.ndarray:
+    """Cache lengths of a decode workload's sequences (int32 [B]): seeded
+    uniform draws in [Tk/8, Tk], the last sequence at the full Tk."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.wid, 99])))
+    lens = g.integers(w.Tk // 8, w.Tk, size=w.B, endpoint=True).astype(np.int32)
+    lens[-1] = w.Tk
+    return lens
 
 
 def head_normal(wid: int, tensor: str, b: int, h: int, rows: int, cols: int, sigma: float = 1.0) -> np.ndarray:

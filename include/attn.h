@@ -183,6 +183,42 @@ int attn_merge_states(const float* acc, const float* m, const float* l, int n, v
                       int B, int H, int Tq, int dv, void* stream);
 
 /*
+ * attn_decode - the newest Tq queries of each sequence against its key/value
+ * cache (the recurrent mode of "The Hidden Recurrence in Softmax Attention",
+ * section "Recurrent mode": the query of step t attends to the keys of steps
+ * up to t; computed as the exact softmax with a running max, "Tiled attention
+ * with an online softmax", section "Task").
+ *   q       : bf16 [B,H,Tq,d], the Tq newest queries of each sequence.
+ *   k, v    : bf16 [B,H,Tk,d] and [B,H,Tk,dv], Tk cache slots per (b, h);
+ *             sequence b uses slots 0 .. L_b-1.
+ *   kv_lens : device int32 [B] holding L_b, or NULL for L_b = Tk.  Values are
+ *             read on the device and clamped to [0, Tk]; slots at L_b and
+ *             beyond are never read.
+ *   o, lse  : bf16 [B,H,Tq,dv] and fp32 [B,H,Tq] outputs.
+ * Query i of sequence b sits at position L_b - Tq + i.  causal != 0: key j is
+ * blocked for it when j > L_b - Tq + i (so the newest query sees every cached
+ * key and query i the keys up to its own position); causal == 0: every key
+ * j < L_b is allowed.  A query with no allowed key gets o = 0, lse = -inf.
+ * 1 <= Tq <= ATTN_DECODE_MAX_QUERIES and d == dv in {64, 128}, else
+ * ATTN_ERR_UNSUPPORTED.  The key range is split over workgroups; with more
+ * than one split the partial states are merged with the rescale rule
+ * ("Chunk-wise Mode with Online Softmax Re-scale"), using a workspace of
+ * splits*B*H*Tq*(dv+2) floats from hipMallocAsync on `stream`.
+ */
+#define ATTN_DECODE_MAX_QUERIES 4
+int attn_decode(const void* q, const void* k, const void* v, const int* kv_lens, void* o, float* lse,
+                int B, int H, int Tq, int Tk, int d, int dv, float scale, int causal, void* stream);
+
+/*
+ * attn_decode_splits - attn_decode with an explicit number of key-range splits
+ * (0: the library's choice, as attn_decode; values above the number of
+ * row batches per sequence are clamped).  Other arguments as attn_decode.
+ */
+int attn_decode_splits(const void* q, const void* k, const void* v, const int* kv_lens, void* o, float* lse,
+                       int B, int H, int Tq, int Tk, int d, int dv, float scale, int causal, int num_splits,
+                       void* stream);
+
+/*
  * attn_fwd_f32 - fp32 forward that follows the page's block loop literally:
  * keys are taken in blocks of `block_n` starting at 0, block_n, 2*block_n, ...
  * (the last may be shorter) and each block updates (m, l, a) with one online
@@ -222,7 +258,8 @@ int attn_bwd_f32(const float* q, const float* k, const float* v, const float* o,
 #define ATTN_KERNEL_BWD_PREP 2       /* D = rowsum(dO o O), LSE*log2(e), transposed K */
 #define ATTN_KERNEL_BWD_DKDV 3       /* backward: dK and dV */
 #define ATTN_KERNEL_BWD_DQ 4         /* backward: dQ */
-#define ATTN_KERNEL_KINDS 5
+#define ATTN_KERNEL_DECODE 5         /* decode main kernel (its split merge counts as ATTN_KERNEL_FWD_AUX) */
+#define ATTN_KERNEL_KINDS 6
 int attn_profile_start(void);
 int attn_profile_stop(void);
 int attn_profile_query(int kind, double* total_ms, int* launches);

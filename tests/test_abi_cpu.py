@@ -121,6 +121,24 @@ def test_merge_states_validates(lib):
     assert lib.attn_merge_states(*a) == attn.ATTN_ERR_UNSUPPORTED
 
 
+def test_decode_validates(lib):
+    # q k v kv_lens o lse B H Tq Tk d dv scale causal stream; kv_lens may be null
+    args = [NZ, NZ, NZ, None, NZ, NZ, 2, 4, 1, 4096, 128, 128, 0.088, 1, None]
+    for i in (0, 1, 2, 4, 5):
+        a = list(args)
+        a[i] = None
+        assert lib.attn_decode(*a) == attn.ATTN_ERR_INVALID_ARG
+    for i, bad in ((6, 0), (8, 0), (9, 0), (12, -1.0), (12, float("nan"))):
+        a = list(args)
+        a[i] = bad
+        assert lib.attn_decode(*a) == attn.ATTN_ERR_INVALID_ARG
+    for i, bad in ((8, attn.DECODE_MAX_QUERIES + 1), (10, 96), (11, 64)):
+        a = list(args)
+        a[i] = bad
+        assert lib.attn_decode(*a) == attn.ATTN_ERR_UNSUPPORTED
+    assert lib.attn_decode_splits(*args[:-1], -1, None) == attn.ATTN_ERR_INVALID_ARG
+
+
 def test_f32_entry_points_validate(lib):
     base = [NZ] * 5 + [1, 1, 8, 8, 64, 64, 0.125, 0]
     assert lib.attn_fwd_f32(*base, -1, None) == attn.ATTN_ERR_INVALID_ARG
