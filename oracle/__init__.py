@@ -6,6 +6,7 @@ from .attention_oracle import (  # noqa: F401
     backward_dkdv_cols,
     backward_dq_rows,
     causal_blocked,
+    chunkwise_unrescaled,
     dense_backward,
     decode_forward,
     dense_forward,

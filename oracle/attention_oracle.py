@@ -42,6 +42,11 @@ full score rows materialised:
   slots of a key cache, query i at position L_b - Tq + i ("The Hidden
   Recurrence in Softmax Attention", section "Recurrent mode": the query of
   step t sees the keys of steps up to t); the plain definition per row.
+* Chunk-wise mode without the rescale.  "The Hidden Recurrence in Softmax
+  Attention", section "Chunk-wise Mode": row sums and accumulators of
+  exp(S) o M added chunk by chunk with no max subtracted.  Exact for modest
+  scores, overflowing for large ones; kept as the negative control that shows
+  why the rescale exists.
 * Gradient of the log-sum-exp.  When a caller also differentiates LSE, its
   upstream gradient dLSE adds dLSE o P to dS, since d LSE_i / d S_ij = P_ij
   ("Flash Attention Backward Pass", which treats l as a smooth function of the
@@ -250,6 +255,37 @@ def decode_forward(q, k, v, scale, kv_lens=None, causal=False):
                 s = np.where(causal_blocked(tq, n, row0=n - tq), NEG_INF, s)
             p, lse[b, h] = _softmax_rows(s)
             o[b, h] = p @ v[b, h, :n]
+    return o, lse
+
+
+# --- Chunk-wise mode without the rescale (negative control) -------------------
+
+def chunkwise_unrescaled(q, k, v, block_size, scale, causal=False):
+    """The chunk-wise mode of "The Hidden Recurrence in Softmax Attention",
+    section "Chunk-wise Mode", before the rescale is introduced: over key
+    chunks of `block_size` (starting at 0, the last possibly shorter) the row
+    sums ll += (exp(S_chunk) o M) 1 and the accumulator A += (exp(S_chunk) o M)
+    V_chunk are added up with no max subtracted; O = A / ll and LSE = ln ll.
+    S = scale * Q K^T; M is the causal mask (key j blocked for query i when
+    j > i) or no mask.  exp overflows to inf once a score passes about 709.78
+    in float64; the result then holds inf or nan, which is the point of this
+    function: it shows what the rescale prevents.  One head: q [Tq, d]."""
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    if block_size < 1:
+        raise ValueError("block_size must be >= 1")
+    tq, tk = q.shape[0], k.shape[0]
+    ll = np.zeros(tq)
+    acc = np.zeros((tq, v.shape[1]))
+    with np.errstate(over="ignore", invalid="ignore"):
+        for start in range(0, tk, block_size):
+            stop = min(start + block_size, tk)
+            e = np.exp(scale * (q @ k[start:stop].T))
+            if causal:
+                e = np.where(causal_blocked(tq, stop - start, col0=start), 0.0, e)
+            ll = ll + np.sum(e, axis=1)
+            acc = acc + e @ v[start:stop]
+        o = acc / ll[:, None]
+        lse = np.log(ll)
     return o, lse
 
 

@@ -268,6 +268,35 @@ def pin_decode(mod):
                 and np.all(np.isfinite(lse[2, :, 2])) and np.allclose(o[2, :, 2], v[2, :, 0]))
 
 
+def pin_chunkwise_unrescaled(mod):
+    """The un-rescaled chunk-wise mode: equal to the dense forward and to the
+    page's token-by-token recurrence for modest scores at every chunk size,
+    and overflowing (inf / nan) where the dense forward stays finite once a
+    score passes the float64 exp range."""
+    r = _rng(71)
+    tq, tk, d, dv = 5, 11, 4, 3
+    q, k, v = r.standard_normal((tq, d)), r.standard_normal((tk, d)), r.standard_normal((tk, dv))
+    for causal in (False, True):
+        ro, rl = mod.dense_forward(q, k, v, 0.6, causal)
+        for b in (1, 2, 3, 11, 20):
+            o, lse = mod.chunkwise_unrescaled(q, k, v, b, 0.6, causal)
+            if not (np.allclose(o, ro, atol=1e-12, rtol=0) and np.allclose(lse, rl, atol=1e-12, rtol=0)):
+                return False
+        for i in range(tq):
+            last = i if causal else tk - 1
+            ro_i, rl_i = _recurrent_mode(q[i], k, v, 0.6, last)
+            o, lse = mod.chunkwise_unrescaled(q, k, v, 4, 0.6, causal)
+            if not (np.allclose(o[i], ro_i, atol=1e-12) and abs(lse[i] - rl_i) < 1e-12):
+                return False
+    big = q.copy()
+    big[:, 0] = 400.0
+    kb = k.copy()
+    kb[:, 0] = 5.0  # scores about 0.6 * 400 * 5 = 1200 > 709.78
+    o, lse = mod.chunkwise_unrescaled(big, kb, v, 4, 0.6, False)
+    ro, rl = mod.dense_forward(big, kb, v, 0.6, False)
+    return bool(np.all(~np.isfinite(o)) and np.all(np.isinf(lse)) and np.all(np.isfinite(ro)) and np.all(np.isfinite(rl)))
+
+
 def pin_block_invariance(mod):
     ok = True
     for seed, tq, tk, d, dv in [(21, 64, 64, 64, 64), (22, 5, 37, 3, 9), (23, 37, 5, 8, 2), (24, 1, 1, 1, 1)]:
@@ -513,6 +542,8 @@ MUTANTS = {
     "merge_weight_inverted": ("w = np.exp(m_s - mu)", "w = np.exp(mu - m_s)"),
     "merge_l_unweighted": ("l = l + w * _as_f64(l_s)", "l = l + _as_f64(l_s)"),
     "decode_query_position_off_by_one": ("causal_blocked(tq, n, row0=n - tq)", "causal_blocked(tq, n, row0=n - tq + 1)"),
+    "chunkwise_drops_causal_mask": ("e = np.where(causal_blocked(tq, stop - start, col0=start), 0.0, e)", "e = e"),
+    "chunkwise_lse_base2": ("lse = np.log(ll)", "lse = np.log2(ll)"),
     "decode_values_misindexed": ("o[b, h] = p @ v[b, h, :n]", "o[b, h] = p @ v[b, h, :n][::-1]"),
 }
 
@@ -540,6 +571,7 @@ def _all_pins_pass(mod, g):
         lambda: pin_torch_dlse(mod),
         lambda: pin_fd_dlse(mod),
         lambda: pin_decode(mod),
+        lambda: pin_chunkwise_unrescaled(mod),
     ]
     for c in checks:
         try:
@@ -558,6 +590,10 @@ def test_dlse_backward_matches_finite_differences_and_torch():
 
 def test_decode_matches_recurrent_mode_and_dense_forward():
     assert pin_decode(ao)
+
+
+def test_unrescaled_chunkwise_mode_exact_then_overflows():
+    assert pin_chunkwise_unrescaled(ao)
 
 
 def test_merged_key_range_states_equal_dense_forward():
