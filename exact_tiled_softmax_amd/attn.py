@@ -22,7 +22,7 @@ ATTN_ERR_UNSUPPORTED = -2
 ATTN_ERR_HIP = -3
 
 EXPORTED = ("attn_fwd", "attn_fwd_splits", "attn_bwd", "attn_bwd_dlse", "attn_fwd_state", "attn_merge_states",
-            "attn_decode", "attn_decode_splits", "attn_fwd_f32", "attn_bwd_f32", "attn_strerror", "attn_last_hip_error", "attn_profile_start",
+            "attn_decode", "attn_decode_splits", "attn_fwd_f32", "attn_fwd_f32_unrescaled", "attn_bwd_f32", "attn_strerror", "attn_last_hip_error", "attn_profile_start",
             "attn_profile_stop", "attn_profile_query")
 
 # kernel kinds of attn_profile_query (include/attn.h)
@@ -63,9 +63,10 @@ def load() -> ctypes.CDLL:
     lib.attn_decode.argtypes = [P, P, P, P, P, P, *dims, P]
     lib.attn_decode_splits.argtypes = [P, P, P, P, P, P, *dims, I, P]
     lib.attn_fwd_f32.argtypes = [P, P, P, P, P, *dims, I, P]
+    lib.attn_fwd_f32_unrescaled.argtypes = [P, P, P, P, P, *dims, I, P]
     lib.attn_bwd_f32.argtypes = [P, P, P, P, P, P, P, P, P, *dims, P]
     for fn in ("attn_fwd", "attn_fwd_splits", "attn_bwd", "attn_bwd_dlse", "attn_fwd_state", "attn_merge_states",
-               "attn_decode", "attn_decode_splits", "attn_fwd_f32", "attn_bwd_f32"):
+               "attn_decode", "attn_decode_splits", "attn_fwd_f32", "attn_fwd_f32_unrescaled", "attn_bwd_f32"):
         getattr(lib, fn).restype = I
     lib.attn_strerror.argtypes = [I]
     lib.attn_strerror.restype = ctypes.c_char_p
@@ -236,8 +237,10 @@ def decode(q, k, v, kv_lens=None, scale=None, causal=False, out=None, lse=None, 
     return out, lse
 
 
-def fwd_f32(q, k, v, scale=None, causal=False, block_n=0, out=None, lse=None):
-    """fp32 forward with the key-block size `block_n` (0 = default)."""
+def fwd_f32(q, k, v, scale=None, causal=False, block_n=0, out=None, lse=None, rescale=True):
+    """fp32 forward with the key-block size `block_n` (0 = default).
+    rescale=False calls attn_fwd_f32_unrescaled (the chunk-wise mode without
+    a running max: a negative control that overflows for large scores)."""
     lib = load()
     B, H, Tq, Tk, d, dv = _dims(q, k, v)
     dev = q.device
@@ -247,9 +250,10 @@ def fwd_f32(q, k, v, scale=None, causal=False, block_n=0, out=None, lse=None):
         scale = 1.0 / math.sqrt(d)
     out = torch.empty((B, H, Tq, dv), dtype=torch.float32, device=dev) if out is None else out
     lse = torch.empty((B, H, Tq), dtype=torch.float32, device=dev) if lse is None else lse
-    rc = lib.attn_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Tq, Tk, d, dv, float(scale),
+    fn = "attn_fwd_f32" if rescale else "attn_fwd_f32_unrescaled"
+    rc = getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Tq, Tk, d, dv, float(scale),
                           int(bool(causal)), int(block_n), _stream(dev))
-    _check("attn_fwd_f32", rc)
+    _check(fn, rc)
     return out, lse
 
 

@@ -277,16 +277,28 @@ int attn_decode_splits(const void* q, const void* k, const void* v, const int* k
   return decode_impl(q, k, v, kv_lens, o, lse, B, H, Tq, Tk, d, dv, scale, causal, num_splits, stream);
 }
 
-int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int Tq, int Tk,
-                 int d, int dv, float scale, int causal, int block_n, void* stream) {
+namespace {
+int fwd_f32_impl(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int Tq, int Tk,
+                 int d, int dv, float scale, int causal, int block_n, int rescale, void* stream) {
   int rc = check_common(q, k, v, o, lse, B, H, Tq, Tk, d, dv, scale);
   if (rc != ATTN_OK) return rc;
   if (d > 128 || dv > 128) return ATTN_ERR_UNSUPPORTED;
   if (block_n < 0 || block_n > 1024) return ATTN_ERR_INVALID_ARG;
   if (block_n == 0) block_n = 64;
-  hipError_t e = attn::fwd_f32_launch(q, k, v, o, lse, B * H, Tq, Tk, d, dv, scale, causal, block_n,
+  hipError_t e = attn::fwd_f32_launch(q, k, v, o, lse, B * H, Tq, Tk, d, dv, scale, causal, block_n, rescale,
                                       static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
+}
+}  // namespace
+
+int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int Tq, int Tk,
+                 int d, int dv, float scale, int causal, int block_n, void* stream) {
+  return fwd_f32_impl(q, k, v, o, lse, B, H, Tq, Tk, d, dv, scale, causal, block_n, 1, stream);
+}
+
+int attn_fwd_f32_unrescaled(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int Tq,
+                            int Tk, int d, int dv, float scale, int causal, int block_n, void* stream) {
+  return fwd_f32_impl(q, k, v, o, lse, B, H, Tq, Tk, d, dv, scale, causal, block_n, 0, stream);
 }
 
 int attn_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* lse, const float* dout,

@@ -48,8 +48,11 @@ hipError_t decode_bf16_launch(const void* q, const void* k, const void* v, const
                               void* workspace, hipStream_t stream);
 
 // ---- fp32 path (block-size faithful forward, deterministic backward) -------------
+// rescale == 0: the chunk-wise mode without the running max (overflows for
+// large scores; a negative control).
 hipError_t fwd_f32_launch(const float* q, const float* k, const float* v, float* o, float* lse, int BH, int Tq,
-                          int Tk, int d, int dv, float scale, int causal, int block_n, hipStream_t stream);
+                          int Tk, int d, int dv, float scale, int causal, int block_n, int rescale,
+                          hipStream_t stream);
 hipError_t bwd_f32_launch(const float* q, const float* k, const float* v, const float* o, const float* lse,
                           const float* dout, float* dq, float* dk, float* dv_grad, int BH, int Tq, int Tk, int d,
                           int dv, float scale, int causal, hipStream_t stream);

@@ -11,6 +11,13 @@
 //   l' = c l + sum_j p_j;  a' = c a + sum_j p_j v_j
 // After the last block the row is a / l and its log-sum-exp m + log l.
 //
+// RESCALE == false is the chunk-wise mode of "The Hidden Recurrence in
+// Softmax Attention" (section "Chunk-wise Mode") before its rescale: the same
+// block loop with no max, l += sum_j exp(s_j), a += sum_j exp(s_j) v_j, and
+// LSE = log l.  fp32 exp overflows once a score passes about 88.7, and the
+// row then turns into inf / nan: a negative control for the rescale, not a
+// path to use.
+//
 // Backward: D_i = sum_c dO_ic O_ic; P_ij = exp(s_ij - LSE_i);
 // dS_ij = P_ij (dO_i . V_j - D_i)  ("attention backprop", "Gradient of S");
 // dQ_i = scale sum_j dS_ij K_j (one wave per query row) and
@@ -41,6 +48,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // one wave (64 threads) per (bh, query row)
+template <bool RESCALE>
 __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                                                      const float* __restrict__ v, float* __restrict__ o,
                                                      float* __restrict__ lse, int Tq, int Tk, int d, int dv,
@@ -72,10 +80,13 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ q
       pblk[j - start] = s;
       bmax = fmaxf(bmax, s);
     }
-    bmax = wave_max(bmax);
-    const float m_new = fmaxf(m, bmax);
-    const float mu = (m_new == -INFINITY) ? 0.f : m_new;
-    const float cfac = expf(m - mu);
+    float m_new = 0.f, mu = 0.f, cfac = 1.f;
+    if (RESCALE) {
+      bmax = wave_max(bmax);
+      m_new = fmaxf(m, bmax);
+      mu = (m_new == -INFINITY) ? 0.f : m_new;
+      cfac = expf(m - mu);
+    }
     float psum = 0.f;
     for (int j = start + lane; j < stop; j += 64) {
       const float p = expf(pblk[j - start] - mu);
@@ -100,7 +111,11 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ q
   float* O = o + (bh * Tq + i) * dv;
   if (lane < dv) O[lane] = acc0 * inv;
   if (lane + 64 < dv) O[lane + 64] = acc1 * inv;
-  if (lane == 0) lse[bh * Tq + i] = l > 0.f ? m + logf(l) : -INFINITY;
+  if (RESCALE) {
+    if (lane == 0) lse[bh * Tq + i] = l > 0.f ? m + logf(l) : -INFINITY;
+  } else {
+    if (lane == 0) lse[bh * Tq + i] = logf(l);  // log 0 = -inf; overflowed rows give inf or nan
+  }
 }
 
 // dQ: one wave per (bh, query row i)
@@ -216,9 +231,15 @@ __global__ __launch_bounds__(64) void bwd_f32_dkdv_kernel(const float* __restric
 }  // namespace
 
 hipError_t fwd_f32_launch(const float* q, const float* k, const float* v, float* o, float* lse, int BH, int Tq,
-                          int Tk, int d, int dv, float scale, int causal, int block_n, hipStream_t stream) {
-  hipLaunchKernelGGL(fwd_f32_kernel, dim3((unsigned)((size_t)BH * Tq)), dim3(64), 0, stream, q, k, v, o, lse, Tq, Tk,
-                     d, dv, scale, causal, block_n);
+                          int Tk, int d, int dv, float scale, int causal, int block_n, int rescale,
+                          hipStream_t stream) {
+  const dim3 grid((unsigned)((size_t)BH * Tq));
+  if (rescale)
+    hipLaunchKernelGGL(fwd_f32_kernel<true>, grid, dim3(64), 0, stream, q, k, v, o, lse, Tq, Tk, d, dv, scale, causal,
+                       block_n);
+  else
+    hipLaunchKernelGGL(fwd_f32_kernel<false>, grid, dim3(64), 0, stream, q, k, v, o, lse, Tq, Tk, d, dv, scale,
+                       causal, block_n);
   return hipGetLastError();
 }
 

@@ -232,6 +232,19 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
                  int block_n, void* stream);
 
 /*
+ * attn_fwd_f32_unrescaled - the chunk-wise mode of "The Hidden Recurrence in
+ * Softmax Attention" (section "Chunk-wise Mode") before the rescale of the
+ * following section: the block loop of attn_fwd_f32 with no running max,
+ *   l += sum_j exp(s_ij),  a += sum_j exp(s_ij) v_j,  o = a / l,  lse = log l.
+ * A NEGATIVE CONTROL, not a path to use: fp32 exp overflows once a score
+ * exceeds about 88.7, and such rows come out inf or nan (attn_fwd_f32 stays
+ * finite on the same input).  Arguments, layouts and errors as attn_fwd_f32.
+ */
+int attn_fwd_f32_unrescaled(const float* q, const float* k, const float* v, float* o, float* lse,
+                            int B, int H, int Tq, int Tk, int d, int dv, float scale, int causal,
+                            int block_n, void* stream);
+
+/*
  * attn_bwd_f32 - fp32 backward (same formulas as attn_bwd, fp32 throughout,
  * deterministic, no workspace).  All tensors fp32.  1 <= d, dv <= 128.
  */

@@ -141,6 +141,12 @@ def test_decode_validates(lib):
 
 def test_f32_entry_points_validate(lib):
     base = [NZ] * 5 + [1, 1, 8, 8, 64, 64, 0.125, 0]
+    for fn in (lib.attn_fwd_f32, lib.attn_fwd_f32_unrescaled):
+        assert fn(*base, -1, None) == attn.ATTN_ERR_INVALID_ARG
+        assert fn(*([None] + base[1:]), 0, None) == attn.ATTN_ERR_INVALID_ARG
+        b = list(base)
+        b[10] = 129
+        assert fn(*b, 0, None) == attn.ATTN_ERR_UNSUPPORTED
     assert lib.attn_fwd_f32(*base, -1, None) == attn.ATTN_ERR_INVALID_ARG
     assert lib.attn_fwd_f32(*base, 1025, None) == attn.ATTN_ERR_INVALID_ARG
     b = list(base)
