@@ -267,6 +267,71 @@ def bench_decode(args, w) -> int:
     return 0
 
 
+def standard_bytes(w):
+    """HBM bytes of the materialised path per call: S written (fp32), read twice
+    by the two-pass row softmax, P written and read (bf16, keys padded to 64),
+    plus Q, K, V read, V^T written and read, O and LSE written."""
+    bh, tkp = w.B * w.H, (w.Tk + 63) // 64 * 64
+    mat = bh * w.Tq * (w.Tk * 4 * 3 + tkp * 2 * 2)
+    io = bh * (2 * (w.Tq * w.d + w.Tk * w.d + w.Tk * w.dv + 2 * tkp * w.dv + w.Tq * w.dv) + 4 * w.Tq)
+    return mat + io
+
+
+def bench_standard(args, w) -> int:
+    """The IO comparison: the tiled forward and the materialised standard
+    forward timed on the same inputs, one after the other."""
+    import torch
+
+    from exact_tiled_softmax_amd import attn
+    from exact_tiled_softmax_amd.inputs import make_tensor
+
+    dev = torch.device("cuda:0")
+    print(f"[bench] building inputs for {w.name}", file=sys.stderr, flush=True)
+    q, k, v = (make_tensor(w, n).to(dev) for n in ("q", "k", "v"))
+    o = torch.empty((w.B, w.H, w.Tq, w.dv), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.H, w.Tq), dtype=torch.float32, device=dev)
+    res = {}
+    for name, fn in (("tiled", attn.fwd), ("standard", attn.fwd_standard)):
+        for _ in range(args.warmup):
+            fn(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse)
+        torch.cuda.synchronize()
+        res[name] = (time.perf_counter() - t0) * 1e3 / args.steps
+        print(f"[bench] {name}: {res[name]:.3f} ms per call", file=sys.stderr, flush=True)
+    _, fwd_fl, _, fwd_b, _ = work(w)
+    std_b = standard_bytes(w)
+    line = {
+        "metric": "attention forward TFLOP/s, tiled vs materialised standard attention (IO comparison)",
+        "value": round(fwd_fl / (res["standard"] * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["standard"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Tq": w.Tq, "Tk": w.Tk, "d": w.d, "dv": w.dv,
+                   "causal": w.causal, "step": "attn_fwd_standard"},
+        "io_comparison": {
+            "tiled_ms": round(res["tiled"], 4),
+            "standard_ms": round(res["standard"], 4),
+            "standard_over_tiled_time": round(res["standard"] / res["tiled"], 2),
+            "tiled_algorithmic_bytes": fwd_b,
+            "standard_hbm_bytes_model": std_b,
+            "standard_over_tiled_bytes": round(std_b / fwd_b, 1),
+            "standard_GBs_at_model": round(std_b / (res["standard"] * 1e-3) / 1e9, 1),
+        },
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -277,6 +342,9 @@ def main(argv=None) -> int:
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the reference kernel "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes) and exit")
+    ap.add_argument("--standard", action="store_true",
+                    help="time the tiled forward and the materialised standard forward (attn_fwd_standard) on the "
+                         "workload and print the IO comparison line instead of the fwd+bwd step")
     ap.add_argument("--decode-splits", type=int, default=0,
                     help="decode workloads: key-range splits per sequence (0 = the library's choice)")
     args = ap.parse_args(argv)
@@ -309,6 +377,8 @@ def main(argv=None) -> int:
         return 2
     if w.decode:
         return bench_decode(args, w)
+    if args.standard:
+        return bench_standard(args, w)
     dev = torch.device("cuda:0")
     print(f"[bench] building inputs for {w.name}", file=sys.stderr, flush=True)
     q, k, v, do = (make_tensor(w, n).to(dev) for n in ("q", "k", "v", "do"))

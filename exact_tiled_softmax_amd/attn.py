@@ -22,7 +22,7 @@ ATTN_ERR_UNSUPPORTED = -2
 ATTN_ERR_HIP = -3
 
 EXPORTED = ("attn_fwd", "attn_fwd_splits", "attn_bwd", "attn_bwd_dlse", "attn_fwd_state", "attn_merge_states",
-            "attn_decode", "attn_decode_splits", "attn_fwd_f32", "attn_fwd_f32_unrescaled", "attn_bwd_f32", "attn_strerror", "attn_last_hip_error", "attn_profile_start",
+            "attn_decode", "attn_decode_splits", "attn_fwd_standard", "attn_fwd_f32", "attn_fwd_f32_unrescaled", "attn_bwd_f32", "attn_strerror", "attn_last_hip_error", "attn_profile_start",
             "attn_profile_stop", "attn_profile_query")
 
 # kernel kinds of attn_profile_query (include/attn.h)
@@ -32,7 +32,8 @@ KERNEL_BWD_PREP = 2
 KERNEL_BWD_DKDV = 3
 KERNEL_BWD_DQ = 4
 KERNEL_DECODE = 5
-KERNEL_NAMES = {0: "fwd", 1: "fwd_aux", 2: "bwd_prep", 3: "bwd_dkdv", 4: "bwd_dq", 5: "decode"}
+KERNEL_STANDARD = 6
+KERNEL_NAMES = {0: "fwd", 1: "fwd_aux", 2: "bwd_prep", 3: "bwd_dkdv", 4: "bwd_dq", 5: "decode", 6: "standard"}
 DECODE_MAX_QUERIES = 4
 
 _lib = None
@@ -61,12 +62,13 @@ def load() -> ctypes.CDLL:
     lib.attn_fwd_state.argtypes = [P, P, P, P, P, P, *dims, I, I, P]
     lib.attn_merge_states.argtypes = [P, P, P, I, P, P, I, I, I, I, P]
     lib.attn_decode.argtypes = [P, P, P, P, P, P, *dims, P]
+    lib.attn_fwd_standard.argtypes = [P, P, P, P, P, *dims, P]
     lib.attn_decode_splits.argtypes = [P, P, P, P, P, P, *dims, I, P]
     lib.attn_fwd_f32.argtypes = [P, P, P, P, P, *dims, I, P]
     lib.attn_fwd_f32_unrescaled.argtypes = [P, P, P, P, P, *dims, I, P]
     lib.attn_bwd_f32.argtypes = [P, P, P, P, P, P, P, P, P, *dims, P]
     for fn in ("attn_fwd", "attn_fwd_splits", "attn_bwd", "attn_bwd_dlse", "attn_fwd_state", "attn_merge_states",
-               "attn_decode", "attn_decode_splits", "attn_fwd_f32", "attn_fwd_f32_unrescaled", "attn_bwd_f32"):
+               "attn_decode", "attn_decode_splits", "attn_fwd_standard", "attn_fwd_f32", "attn_fwd_f32_unrescaled", "attn_bwd_f32"):
         getattr(lib, fn).restype = I
     lib.attn_strerror.argtypes = [I]
     lib.attn_strerror.restype = ctypes.c_char_p
@@ -203,6 +205,26 @@ def merge_states(acc, m, l):
     rc = lib.attn_merge_states(_ptr(acc), _ptr(m), _ptr(l), n, _ptr(o), _ptr(lse), B, H, Tq, dv, _stream(dev))
     _check("attn_merge_states", rc)
     return o, lse
+
+
+def fwd_standard(q, k, v, scale=None, causal=False, out=None, lse=None):
+    """Standard attention with the score matrix materialised in HBM (bf16 in
+    and out, as fwd): returns (o, lse).  For the IO comparison."""
+    lib = load()
+    B, H, Tq, Tk, d, dv = _dims(q, k, v)
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, torch.bfloat16, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty((B, H, Tq, dv), dtype=torch.bfloat16, device=dev) if out is None else out
+    lse = torch.empty((B, H, Tq), dtype=torch.float32, device=dev) if lse is None else lse
+    _need(out, "out", torch.bfloat16, dev)
+    _need(lse, "lse", torch.float32, dev)
+    rc = lib.attn_fwd_standard(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Tq, Tk, d, dv, float(scale),
+                               int(bool(causal)), _stream(dev))
+    _check("attn_fwd_standard", rc)
+    return out, lse
 
 
 def decode(q, k, v, kv_lens=None, scale=None, causal=False, out=None, lse=None, num_splits=None):

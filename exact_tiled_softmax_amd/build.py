@@ -23,7 +23,7 @@ BUILD = os.path.join(PKG, "_build")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
 
-SOURCES = ["api.cpp", "fwd_bf16.hip", "bwd_bf16.hip", "decode_bf16.hip", "ref_f32.hip"]
+SOURCES = ["api.cpp", "fwd_bf16.hip", "bwd_bf16.hip", "decode_bf16.hip", "standard_bf16.hip", "ref_f32.hip"]
 ARCH = os.environ.get("ATTN_OFFLOAD_ARCH", "gfx950")
 
 

@@ -267,6 +267,22 @@ int attn_merge_states(const float* acc, const float* m, const float* l, int n, v
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
 }
 
+int attn_fwd_standard(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Tq, int Tk,
+                      int d, int dv, float scale, int causal, void* stream) {
+  int rc = check_common(q, k, v, o, lse, B, H, Tq, Tk, d, dv, scale);
+  if (rc != ATTN_OK) return rc;
+  if (!bf16_dims_supported(d, dv)) return ATTN_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int BH = B * H;
+  void* ws = nullptr;
+  hipError_t e = hipMallocAsync(&ws, attn::std_bf16_workspace_bytes(BH, Tq, Tk, d), s);
+  if (e != hipSuccess) return hip_fail(e);
+  e = attn::std_bf16_launch(q, k, v, o, lse, BH, Tq, Tk, d, scale, causal, ws, s);
+  hipError_t f = hipFreeAsync(ws, s);
+  if (e == hipSuccess) e = f;
+  return e == hipSuccess ? ATTN_OK : hip_fail(e);
+}
+
 int attn_decode(const void* q, const void* k, const void* v, const int* kv_lens, void* o, float* lse, int B, int H,
                 int Tq, int Tk, int d, int dv, float scale, int causal, void* stream) {
   return decode_impl(q, k, v, kv_lens, o, lse, B, H, Tq, Tk, d, dv, scale, causal, 0, stream);

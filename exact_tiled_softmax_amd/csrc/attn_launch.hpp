@@ -47,6 +47,11 @@ hipError_t decode_bf16_launch(const void* q, const void* k, const void* v, const
                               int B, int H, int Tq, int Tk, int d, float scale, int causal, int num_splits,
                               void* workspace, hipStream_t stream);
 
+// ---- bf16 standard (materialised) attention, for the IO comparison -------------
+size_t std_bf16_workspace_bytes(int BH, int Tq, int Tk, int d);
+hipError_t std_bf16_launch(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Tq, int Tk,
+                           int d, float scale, int causal, void* workspace, hipStream_t stream);
+
 // ---- fp32 path (block-size faithful forward, deterministic backward) -------------
 // rescale == 0: the chunk-wise mode without the running max (overflows for
 // large scores; a negative control).

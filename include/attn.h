@@ -183,6 +183,20 @@ int attn_merge_states(const float* acc, const float* m, const float* l, int n, v
                       int B, int H, int Tq, int dv, void* stream);
 
 /*
+ * attn_fwd_standard - standard attention with the score matrix materialised
+ * in HBM ("The Hidden Recurrence in Softmax Attention", section "Standard
+ * Attention / Forward Pass"): S = scale Q K^T (fp32, blocked keys -inf), the
+ * row softmax P (bf16) with LSE, then O = P V, each step a kernel of its own.
+ * Same arguments, outputs and supported sizes as attn_fwd; the results agree
+ * with attn_fwd to bf16 rounding.  For measuring what the tiled method saves:
+ * it takes a workspace of about B*H*Tq*Tk*6 bytes (S in fp32 and P in bf16)
+ * from hipMallocAsync on `stream` (ATTN_ERR_HIP if that fails) and moves
+ * Tq*Tk*12 bytes per head through HBM.
+ */
+int attn_fwd_standard(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int H, int Tq, int Tk, int d, int dv, float scale, int causal, void* stream);
+
+/*
  * attn_decode - the newest Tq queries of each sequence against its key/value
  * cache (the recurrent mode of "The Hidden Recurrence in Softmax Attention",
  * section "Recurrent mode": the query of step t attends to the keys of steps
@@ -272,7 +286,8 @@ int attn_bwd_f32(const float* q, const float* k, const float* v, const float* o,
 #define ATTN_KERNEL_BWD_DKDV 3       /* backward: dK and dV */
 #define ATTN_KERNEL_BWD_DQ 4         /* backward: dQ */
 #define ATTN_KERNEL_DECODE 5         /* decode main kernel (its split merge counts as ATTN_KERNEL_FWD_AUX) */
-#define ATTN_KERNEL_KINDS 6
+#define ATTN_KERNEL_STANDARD 6       /* attn_fwd_standard: its kernels together */
+#define ATTN_KERNEL_KINDS 7
 int attn_profile_start(void);
 int attn_profile_stop(void);
 int attn_profile_query(int kind, double* total_ms, int* launches);

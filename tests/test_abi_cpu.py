@@ -121,6 +121,22 @@ def test_merge_states_validates(lib):
     assert lib.attn_merge_states(*a) == attn.ATTN_ERR_UNSUPPORTED
 
 
+def test_fwd_standard_validates(lib):
+    args = [NZ] * 5 + [1, 2, 64, 64, 128, 128, 0.088, 1, None]
+    for i in range(5):
+        a = list(args)
+        a[i] = None
+        assert lib.attn_fwd_standard(*a) == attn.ATTN_ERR_INVALID_ARG
+    for i, bad in ((5, 0), (7, 0), (11, float("inf"))):
+        a = list(args)
+        a[i] = bad
+        assert lib.attn_fwd_standard(*a) == attn.ATTN_ERR_INVALID_ARG
+    a = list(args)
+    a[9] = 96
+    a[10] = 96
+    assert lib.attn_fwd_standard(*a) == attn.ATTN_ERR_UNSUPPORTED
+
+
 def test_decode_validates(lib):
     # q k v kv_lens o lse B H Tq Tk d dv scale causal stream; kv_lens may be null
     args = [NZ, NZ, NZ, None, NZ, NZ, 2, 4, 1, 4096, 128, 128, 0.088, 1, None]
