@@ -38,6 +38,8 @@
 // 16-byte row reads and transposing reads are free of bank conflicts, and
 // tiles are copied global -> LDS by the direct-to-LDS vector load, several
 // tiles ahead of the compute.
+#include <algorithm>
+
 #include "attn_common.hpp"
 #include "attn_launch.hpp"
 #include "tile_stream.hpp"
@@ -56,7 +58,9 @@ struct BwdArgs {
   __bf16* dq;
   __bf16* dk;
   __bf16* dv;
+  float* dq_part;      // [dq_splits][BH][Tq][D] fp32 when the dQ key range is split
   int BH, Tq, Tk, Tk_pad, nqb32;
+  int dq_splits, dq_tiles_per_split;  // key-range split of the dQ kernel (64-key tiles per split)
   float scale, scale_log2;
 };
 
@@ -465,7 +469,11 @@ __device__ __forceinline__ void dq_compute(const BwdArgs& a, DqWave& w, const __
   }
 }
 
-template <int D, bool CAUSAL>
+// SPLIT: the workgroup covers key tiles [split * dq_tiles_per_split, ...) of
+// its query block and writes an fp32 partial dQ (scaled) that dq_reduce_kernel
+// sums over the splits in a fixed order; every split writes its partial,
+// zeros when its range holds no key of the block.
+template <int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a) {
   using C = DqCfg<D>;
   __shared__ __attribute__((aligned(1024))) __bf16 stg0[C::STAGE];
@@ -476,9 +484,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   const int lr = lane % 32, hf = lane / 32;
   const int nqb = (a.Tq + C::BM - 1) / C::BM;
-  const int item = xcd_remap(blockIdx.x, a.BH * nqb);
-  const int bh = item / nqb;
-  const int qb = CAUSAL ? nqb - 1 - item % nqb : item % nqb;  // most causal work first within a head
+  const int ns = SPLIT ? a.dq_splits : 1;
+  const int item = xcd_remap(blockIdx.x, a.BH * nqb * ns);
+  const int split = item % ns;
+  const int bh = item / (nqb * ns);
+  const int qi = (item / ns) % nqb;
+  const int qb = CAUSAL ? nqb - 1 - qi : qi;  // most causal work first within a head
   const int q0 = qb * C::BM;
   const int qw = q0 + 32 * wave;
   const int my_q = qw + lr;
@@ -513,28 +524,44 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a) {
 
   const int nkt_all = (a.Tk + 63) / 64;
   const int last_q = min(q0 + C::BM - 1, a.Tq - 1);
-  const int n = CAUSAL ? min(nkt_all, last_q / 64 + 1) : nkt_all;
+  const int n_all = CAUSAL ? min(nkt_all, last_q / 64 + 1) : nkt_all;
+  // this workgroup's key tiles: [jb, jb + n)
+  const int jb = SPLIT ? min(n_all, split * a.dq_tiles_per_split) : 0;
+  const int n = SPLIT ? min(n_all - jb, a.dq_tiles_per_split) : n_all;
   // keys this wave needs: [0, kend)
   const int kend = qw >= a.Tq ? 0 : (CAUSAL ? min(a.Tk, min(qw + 31, a.Tq - 1) + 1) : a.Tk);
 
-  // tiles 0, 1 in flight before the loop; tile j+2 is issued at step j
-  if (n > 0) dq_issue<D>(a, bh, 0, stg0, wave, lane);
-  if (n > 1) dq_issue<D>(a, bh, 1, stg1, wave, lane);
+  // local tiles 0, 1 in flight before the loop; local tile i+2 is issued at step i
+  if (n > 0) dq_issue<D>(a, bh, jb, stg0, wave, lane);
+  if (n > 1) dq_issue<D>(a, bh, jb + 1, stg1, wave, lane);
 
-  auto step = [&](int j, const __bf16* cur, __bf16* ahead) {
-    if (j + 1 < n) wait_vm<C::VM>();
+  auto step = [&](int i, const __bf16* cur, __bf16* ahead) {
+    if (i + 1 < n) wait_vm<C::VM>();
     else wait_vm<0>();
     barrier();
-    if (j + 2 < n) dq_issue<D>(a, bh, j + 2, ahead, wave, lane);
-    if (64 * j < kend) dq_compute<D, CAUSAL>(a, w, cur, j, qw, kend, lane);
+    if (i + 2 < n) dq_issue<D>(a, bh, jb + i + 2, ahead, wave, lane);
+    if (64 * (jb + i) < kend) dq_compute<D, CAUSAL>(a, w, cur, jb + i, qw, kend, lane);
   };
-  for (int j = 0; j < n; j += 3) {
-    step(j, stg0, stg2);
-    if (j + 1 < n) step(j + 1, stg1, stg0);
-    if (j + 2 < n) step(j + 2, stg2, stg1);
+  for (int i = 0; i < n; i += 3) {
+    step(i, stg0, stg2);
+    if (i + 1 < n) step(i + 1, stg1, stg0);
+    if (i + 2 < n) step(i + 2, stg2, stg1);
   }
 
   // dQ = scale * (dQ^T)^T: register r of block cb is column 32cb + 8(r/4) + 4hf + r%4
+  if (SPLIT) {
+    if (my_q < a.Tq) {
+      float* pr = a.dq_part + (((size_t)split * a.BH + bh) * a.Tq + my_q) * D;
+#pragma unroll
+      for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<f32x4*>(pr + 32 * cb + 8 * g + 4 * hf) =
+              f32x4{w.dqt[cb][4 * g] * a.scale, w.dqt[cb][4 * g + 1] * a.scale, w.dqt[cb][4 * g + 2] * a.scale,
+                    w.dqt[cb][4 * g + 3] * a.scale};
+    }
+    return;
+  }
   if (my_q < a.Tq) {
     __bf16* dqr = a.dq + ((size_t)bh * a.Tq + my_q) * D;
 #pragma unroll
@@ -548,19 +575,53 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a) {
   }
 }
 
+// dQ = sum over the key-range splits of the partials, in split order; four
+// values per thread.
+__global__ __launch_bounds__(256) void dq_reduce_kernel(const float* __restrict__ part, __bf16* __restrict__ dq,
+                                                        size_t n4, int splits) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n4) return;
+  const f32x4* p = reinterpret_cast<const f32x4*>(part) + i;
+  f32x4 acc = p[0];
+  for (int s = 1; s < splits; ++s) acc += p[(size_t)s * n4];
+  *reinterpret_cast<u32x2*>(dq + 4 * i) = u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+}
+
 // ---------------------------------------------------------------------------------
+// Key-range splits of the dQ kernel: only when the query blocks alone leave the
+// CUs under-filled (fewer than two workgroups per CU), about 1024 workgroups
+// then, each split at least 8 key tiles (512 keys) long.
+struct DqSplit {
+  int splits, tiles_per_split;
+};
+
+DqSplit dq_split(int BH, int Tq, int Tk) {
+  const int nqb = (Tq + 255) / 256;
+  const int nkt = (Tk + 63) / 64;
+  const long long items = (long long)BH * nqb;
+  int s = 1;
+  if (items < 512) {
+    s = (int)((1024 + items - 1) / items);
+    s = std::min(s, std::max(1, nkt / 8));
+  }
+  const int tps = (nkt + s - 1) / s;
+  return {(nkt + tps - 1) / tps, tps};
+}
+
 struct BwdLayout {
-  size_t stats, kt, total;
+  size_t stats, kt, dq_part, total;
 };
 
 BwdLayout bwd_layout(int BH, int Tq, int Tk, int d) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   const size_t nqb32 = (size_t)(Tq + 31) / 32;
   const size_t tk_pad = (size_t)(Tk + 63) / 64 * 64;
+  const DqSplit sp = dq_split(BH, Tq, Tk);
   BwdLayout L;
   L.stats = 0;
   L.kt = up(L.stats + (size_t)BH * nqb32 * 64 * sizeof(float));
-  L.total = up(L.kt + (size_t)BH * d * tk_pad * 2);
+  L.dq_part = up(L.kt + (size_t)BH * d * tk_pad * 2);
+  L.total = L.dq_part + (sp.splits > 1 ? up((size_t)sp.splits * BH * Tq * d * sizeof(float)) : 0);
   return L;
 }
 
@@ -591,11 +652,23 @@ hipError_t bwd_launch_d(BwdArgs& args, const __bf16* o, const float* lse, const 
   if (e != hipSuccess) return e;
 
   const int nqb = (args.Tq + DqCfg<D>::BM - 1) / DqCfg<D>::BM;
+  const int ns = args.dq_splits;
   prof_begin(4, stream);
-  if (causal)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3(args.BH * nqb), dim3(512), 0, stream, args);
-  else
-    hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3(args.BH * nqb), dim3(512), 0, stream, args);
+  const dim3 grid((unsigned)(args.BH * nqb * ns));
+  if (ns > 1) {
+    if (causal)
+      hipLaunchKernelGGL((bwd_dq_kernel<D, true, true>), grid, dim3(512), 0, stream, args);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<D, false, true>), grid, dim3(512), 0, stream, args);
+    const size_t n4 = (size_t)args.BH * args.Tq * D / 4;
+    hipLaunchKernelGGL(dq_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, args.dq_part,
+                       args.dq, n4, ns);
+  } else {
+    if (causal)
+      hipLaunchKernelGGL((bwd_dq_kernel<D, true, false>), grid, dim3(512), 0, stream, args);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<D, false, false>), grid, dim3(512), 0, stream, args);
+  }
   prof_end(4, stream);
   return hipGetLastError();
 }
@@ -624,6 +697,10 @@ hipError_t bwd_bf16_launch(const void* q, const void* k, const void* v, const vo
   a.Tk = Tk;
   a.Tk_pad = (Tk + 63) / 64 * 64;
   a.nqb32 = (Tq + 31) / 32;
+  const DqSplit sp = dq_split(BH, Tq, Tk);
+  a.dq_splits = sp.splits;
+  a.dq_tiles_per_split = sp.tiles_per_split;
+  a.dq_part = sp.splits > 1 ? reinterpret_cast<float*>(ws + L.dq_part) : nullptr;
   a.scale = scale;
   a.scale_log2 = scale * kLog2e;
   const __bf16* ob = static_cast<const __bf16*>(o);

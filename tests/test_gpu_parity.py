@@ -176,6 +176,24 @@ def test_bf16_bwd_small(dev, shape, causal):
     assert_close("dV", f64(dv), rv, TOL_BF16)
 
 
+# Few query blocks and many keys: the dQ kernel splits its key range over
+# workgroups and sums fp32 partials (including empty causal ranges).
+@pytest.mark.parametrize("shape", [(1, 2, 130, 3000, 128, 128), (1, 1, 256, 5000, 64, 64), (2, 1, 40, 1300, 128, 128)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_bwd_long_keys_split_dq(dev, shape, causal):
+    q, k, v, do = bf16_problem(shape, seed=8)
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    o, lse = attn.fwd(qd, kd, vd, causal=causal)
+    dq, dk, dv = attn.bwd(qd, kd, vd, o, lse, dod, causal=causal)
+    dq2, _, _ = attn.bwd(qd, kd, vd, o, lse, dod, causal=causal)
+    torch.cuda.synchronize()
+    rq, rk, rv = dense_backward(f64(q), f64(k), f64(v), f64(do), 1 / np.sqrt(shape[4]), causal)
+    assert_close("dQ", f64(dq), rq, TOL_BF16)
+    assert_close("dK", f64(dk), rk, TOL_BF16)
+    assert_close("dV", f64(dv), rv, TOL_BF16)
+    assert torch.equal(dq.view(torch.int16), dq2.view(torch.int16))  # fixed summation order
+
+
 def test_bf16_inputs_unchanged_and_results_deterministic(dev):
     q, k, v, do = bf16_problem((1, 2, 300, 333, 128, 128), seed=9)
     qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
