@@ -246,14 +246,8 @@ int attn_fwd_state(const void* q, const void* k, const void* v, float* acc, floa
   const long long diag = (long long)q_offset - (long long)k_offset;
   const long long lim = 1LL << 30;
   const int diag_c = (int)(diag > lim ? lim : (diag < -lim ? -lim : diag));
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int BH = B * H;
-  void* ws = nullptr;
-  hipError_t e = hipMallocAsync(&ws, attn::fwd_bf16_state_workspace_bytes(BH, Tq, Tk, d), s);
-  if (e != hipSuccess) return hip_fail(e);
-  e = attn::fwd_bf16_state_launch(q, k, v, acc, m, l, BH, Tq, Tk, d, scale, causal, diag_c, ws, s);
-  hipError_t f = hipFreeAsync(ws, s);
-  if (e == hipSuccess) e = f;
+  hipError_t e = attn::fwd_bf16_state_launch(q, k, v, acc, m, l, B * H, Tq, Tk, d, scale, causal, diag_c,
+                                             static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
 }
 

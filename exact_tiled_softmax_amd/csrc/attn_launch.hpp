@@ -23,10 +23,9 @@ hipError_t fwd_bf16_launch(const void* q, const void* k, const void* v, void* o,
                            hipStream_t stream);
 // Partial state (acc, m, l) of one key range; causal blocks key j for query i
 // when j > i + diag.  m in natural-log units.
-size_t fwd_bf16_state_workspace_bytes(int BH, int Tq, int Tk, int d);
+// (no workspace)
 hipError_t fwd_bf16_state_launch(const void* q, const void* k, const void* v, float* acc, float* m, float* l, int BH,
-                                 int Tq, int Tk, int d, float scale, int causal, int diag, void* workspace,
-                                 hipStream_t stream);
+                                 int Tq, int Tk, int d, float scale, int causal, int diag, hipStream_t stream);
 // Merge of n partial states [n][BH][Tq](x d) into O (bf16) and LSE.
 hipError_t merge_states_launch(const float* acc, const float* m, const float* l, int n, void* o, float* lse, int BH,
                                int Tq, int d, hipStream_t stream);

@@ -7,10 +7,11 @@
 // tiles outside, key tiles inside).  Each wave owns 32 rows and keeps, per
 // row, the running max m, running sum l and accumulator a of "Tiled attention
 // with an online softmax", section "Task", in registers; its Q rows stay in
-// registers as MFMA operands.  K and V^T are streamed in tiles of 64 keys
-// through a 4-stage LDS ring filled by direct-to-LDS copies, three tiles
-// ahead of the compute (V^T is a transposed copy of V made first, in the
-// workspace).
+// registers as MFMA operands.  K and V are streamed, row-major, in tiles of
+// 64 keys through a 4-stage LDS ring filled by direct-to-LDS copies, three
+// tiles ahead of the compute; the V operand of the PV product (V^T, keys
+// along k) comes from transposing LDS reads (ds_read_b64_tr_b16), so no
+// transposed copy of V is made in HBM.
 //
 // Per 64-key tile and wave:
 //   S^T = K Q^T           32x32x16 bf16 MFMA, fp32 accumulators, keys on the
@@ -20,7 +21,8 @@
 //   mask                  causal (key > query) and ragged tails -> blocked
 //                         (diagonal and tail tiles only)
 //   m  = max(m, rowmax)   scores in log2 units (multiplied by scale*log2(e))
-//   P  = exp2(s - m), l += rowsum(P), a += V^T P^T  (P rounded to bf16)
+//   P  = exp2(s - m), l += rowsum(P), a += V^T P^T  (P rounded to bf16; V^T
+//                         fragments by transposing reads of the V tile)
 // Epilogue: O = a / l, LSE = (m + log2 l) * ln 2.
 //
 // The reference max m used in the exponent is only moved when a row's tile
@@ -67,7 +69,7 @@ struct FwdCfg {
 struct FwdArgs {
   const __bf16* q;
   const __bf16* k;
-  const __bf16* vt;  // V^T [BH][D][Tk_pad], keys of each 16-key group in group_row order
+  const __bf16* v;   // V [BH][Tk][D]: row-major tiles in LDS, read transposed
   __bf16* o;
   float* lse;
   float* part_acc;  // [splits][BH][Tq][D]   (split / state mode: unnormalised a)
@@ -79,26 +81,22 @@ struct FwdArgs {
   float scale_log2;  // scale * log2(e)
 };
 
-// Copies of one K tile and one V^T tile (keys key0 .. key0+63) into a stage.
+// Copies of one K tile and one V tile (keys key0 .. key0+63, both row-major,
+// 16-byte chunks swizzled per row) into a stage.
 template <int D>
 __device__ __forceinline__ void fwd_issue(const FwdArgs& a, int bh, int key0, __bf16* stg, int wave, int lane) {
   using C = FwdCfg<D>;
   const __bf16* Kh = a.k + (size_t)bh * a.Tk * D;
-  const __bf16* VTh = a.vt + (size_t)bh * D * a.Tk_pad;
+  const __bf16* Vh = a.v + (size_t)bh * a.Tk * D;
 #pragma unroll
   for (int n = 0; n < C::PER_WAVE; ++n) {
     const int cpy = wave * C::PER_WAVE + n;  // wave-uniform
     const int tensor = cpy / C::PER_TENSOR, i = cpy % C::PER_TENSOR;
     const int p = 64 * i + lane;
     __bf16* dst = stg + tensor * C::TILE + 512 * i;
-    if (tensor == 0) {
-      const int row = p / C::CPR, c = (p % C::CPR) ^ swz<C::CPR>(row);
-      const int kk = min(key0 + row, a.Tk - 1);
-      dma16(Kh + (size_t)kk * D + 8 * c, dst);
-    } else {
-      const int rt = p / 8, ct = (p % 8) ^ swz<8>(rt);
-      dma16(VTh + (size_t)rt * a.Tk_pad + key0 + 8 * ct, dst);
-    }
+    const int row = p / C::CPR, c = (p % C::CPR) ^ swz<C::CPR>(row);
+    const int kk = min(key0 + row, a.Tk - 1);
+    dma16((tensor == 0 ? Kh : Vh) + (size_t)kk * D + 8 * c, dst);
   }
 }
 
@@ -116,8 +114,8 @@ __device__ __forceinline__ void fwd_tile(const __bf16* stg, const bf16x8 (&qf)[8
   using C = FwdCfg<D>;
   const int lr = lane % 32, hf = lane / 32;
   const __bf16* Ks = stg;
-  const __bf16* VTs = stg + C::TILE;
-  const int rsw = swz<C::CPR>(lr), tsw = swz<8>(lr);
+  const __bf16* Vs = stg + C::TILE;
+  const int rsw = swz<C::CPR>(lr);
   // the two 32-key score chains alternate
   f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
@@ -169,13 +167,23 @@ __device__ __forceinline__ void fwd_tile(const __bf16* stg, const bf16x8 (&qf)[8
     }
   l_run += psum;
   // ---- a += V^T P^T -----------------------------------------------------------------
+  // A operand (column 32cb + lane%32 of V, k-slots = the keys of P's k-slots)
+  // by two transposing reads of the row-major V tile: rows 32u + 16s2 + 4hf
+  // + 0..3 and the same + 8 (the order in which the score accumulator hands
+  // its keys to P's k-slots)
+  const int g16 = lane % 16, csub = (lane / 16) % 2;
+  auto at = [](int r, int cc) { return r * D + 8 * ((cc >> 3) ^ swz<C::CPR>(r)) + (cc & 7); };
 #pragma unroll
   for (int u = 0; u < 2; ++u)
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int cb = 0; cb < C::CB; ++cb)
-        acc[cb] = mfma32(ld16(VTs + (32 * cb + lr) * 64 + 8 * ((4 * u + 2 * s2 + hf) ^ tsw)), pb[u][s2], acc[cb]);
+      for (int cb = 0; cb < C::CB; ++cb) {
+        const int r0 = 32 * u + 16 * s2 + 4 * hf + g16 / 4;
+        const int c0 = 32 * cb + 16 * csub + 4 * (g16 % 4);
+        const bf16x8 va = join_tr(lds_read_tr(Vs + at(r0, c0)), lds_read_tr(Vs + at(r0 + 8, c0)));
+        acc[cb] = mfma32(va, pb[u][s2], acc[cb]);
+      }
 }
 
 template <int D, bool CAUSAL, bool SPLIT>
@@ -341,15 +349,15 @@ constexpr int kBN = 64;
 static_assert(FwdCfg<64>::BM == kBM && FwdCfg<128>::BM == kBM && FwdCfg<128>::BN == kBN, "tile sizes");
 
 struct FwdLayout {
-  size_t vt, part_acc, part_m, part_l, total;
+  size_t part_acc, part_m, part_l, total;
 };
 
+// workspace: the key-split partial states only (none without splits)
 FwdLayout fwd_layout(int BH, int Tq, int Tk, int d, int num_splits) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-  const size_t tk_pad = (size_t)(Tk + kBN - 1) / kBN * kBN;
+  (void)Tk;
   FwdLayout L;
-  L.vt = 0;
-  L.part_acc = up((size_t)BH * d * tk_pad * 2);
+  L.part_acc = 0;
   L.part_m = L.part_l = L.total = L.part_acc;
   if (num_splits > 1) {
     L.part_m = up(L.part_acc + (size_t)num_splits * BH * Tq * d * sizeof(float));
@@ -385,12 +393,12 @@ size_t fwd_bf16_workspace_bytes(int BH, int Tq, int Tk, int d, int num_splits) {
 
 namespace {
 
-FwdArgs fwd_args(const void* q, const void* k, void* o, float* lse, int BH, int Tq, int Tk, float scale,
-                 int num_splits, int diag, const void* vt) {
+FwdArgs fwd_args(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Tq, int Tk,
+                 float scale, int num_splits, int diag) {
   FwdArgs args;
   args.q = static_cast<const __bf16*>(q);
   args.k = static_cast<const __bf16*>(k);
-  args.vt = static_cast<const __bf16*>(vt);
+  args.v = static_cast<const __bf16*>(v);
   args.o = static_cast<__bf16*>(o);
   args.lse = lse;
   args.part_acc = args.part_m = args.part_l = nullptr;
@@ -407,18 +415,7 @@ FwdArgs fwd_args(const void* q, const void* k, void* o, float* lse, int BH, int 
   return args;
 }
 
-// V^T copy (profiled as the forward's auxiliary work), then the main kernel.
-hipError_t fwd_run(const FwdArgs& args, const void* v, void* vt, int d, bool causal, bool split, hipStream_t stream) {
-  prof_begin(1, stream);
-  if (d == 128)
-    hipLaunchKernelGGL(transpose_rows_kernel<128>, dim3(args.Tk_pad / 64, args.BH), dim3(256), 0, stream,
-                       static_cast<const __bf16*>(v), static_cast<__bf16*>(vt), args.Tk, args.Tk_pad);
-  else
-    hipLaunchKernelGGL(transpose_rows_kernel<64>, dim3(args.Tk_pad / 64, args.BH), dim3(256), 0, stream,
-                       static_cast<const __bf16*>(v), static_cast<__bf16*>(vt), args.Tk, args.Tk_pad);
-  prof_end(1, stream);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+hipError_t fwd_run(const FwdArgs& args, int d, bool causal, bool split, hipStream_t stream) {
   return (d == 128) ? fwd_dispatch<128>(args, causal, split, stream) : fwd_dispatch<64>(args, causal, split, stream);
 }
 
@@ -443,29 +440,25 @@ hipError_t fwd_bf16_launch(const void* q, const void* k, const void* v, void* o,
                            hipStream_t stream) {
   const FwdLayout L = fwd_layout(BH, Tq, Tk, d, num_splits);
   char* ws = static_cast<char*>(workspace);
-  FwdArgs args = fwd_args(q, k, o, lse, BH, Tq, Tk, scale, num_splits, 0, ws + L.vt);
+  FwdArgs args = fwd_args(q, k, v, o, lse, BH, Tq, Tk, scale, num_splits, 0);
   const bool split = num_splits > 1;
   if (split) {
     args.part_acc = reinterpret_cast<float*>(ws + L.part_acc);
     args.part_m = reinterpret_cast<float*>(ws + L.part_m);
     args.part_l = reinterpret_cast<float*>(ws + L.part_l);
   }
-  hipError_t e = fwd_run(args, v, ws + L.vt, d, causal != 0, split, stream);
+  hipError_t e = fwd_run(args, d, causal != 0, split, stream);
   if (e != hipSuccess || !split) return e;
   return merge_states_launch(args.part_acc, args.part_m, args.part_l, num_splits, o, lse, BH, Tq, d, stream);
 }
 
-size_t fwd_bf16_state_workspace_bytes(int BH, int Tq, int Tk, int d) { return fwd_layout(BH, Tq, Tk, d, 1).total; }
-
 hipError_t fwd_bf16_state_launch(const void* q, const void* k, const void* v, float* acc, float* m, float* l, int BH,
-                                 int Tq, int Tk, int d, float scale, int causal, int diag, void* workspace,
-                                 hipStream_t stream) {
-  char* ws = static_cast<char*>(workspace);
-  FwdArgs args = fwd_args(q, k, nullptr, nullptr, BH, Tq, Tk, scale, 1, diag, ws);
+                                 int Tq, int Tk, int d, float scale, int causal, int diag, hipStream_t stream) {
+  FwdArgs args = fwd_args(q, k, v, nullptr, nullptr, BH, Tq, Tk, scale, 1, diag);
   args.part_acc = acc;
   args.part_m = m;
   args.part_l = l;
-  return fwd_run(args, v, ws, d, causal != 0, true, stream);
+  return fwd_run(args, d, causal != 0, true, stream);
 }
 
 }  // namespace attn

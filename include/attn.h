@@ -45,8 +45,8 @@
  * Stream.   `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *           enqueue work on it and never synchronise; kernel faults surface at
  *           the caller's next synchronisation on that stream.
- * Workspace. attn_fwd and attn_bwd need scratch memory (transposed copies
- *           of V or K, row statistics, split partial states).  The library
+ * Workspace. Some calls need scratch memory (the transposed copy of K and
+ *           row statistics of the backward, split partial states).  The library
  *           takes it with hipMallocAsync on `stream` and returns it with
  *           hipFreeAsync on the same stream, so its lifetime is
  *           stream-ordered and no state persists between calls.
@@ -78,8 +78,8 @@ extern "C" {
  * statistics are fp32; P is rounded to bf16 before the P V product.
  * Supported: d == dv, d in {64, 128}; otherwise ATTN_ERR_UNSUPPORTED.
  * B, H, Tq, Tk >= 1 (any value; ragged tails are masked).
- * Workspace: a transposed copy of V (B*H*dv*Tk*2 bytes, Tk rounded up to 64)
- * plus, with key splits, the partial states.
+ * Workspace: none, except the partial states when the key range is split
+ * (num_splits*B*H*Tq*(dv+2) floats).
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int H, int Tq, int Tk, int d, int dv, float scale, int causal,
@@ -162,7 +162,7 @@ int attn_bwd_dlse(const void* q, const void* k, const void* v, const void* o, co
  *               first key; with causal != 0, key j is blocked for query i when
  *               k_offset + j > q_offset + i (the top-left rule of attn_fwd on
  *               global indices).  Ignored when causal == 0.
- * Supported: d == dv, d in {64, 128}.  Workspace: a transposed copy of v.
+ * Supported: d == dv, d in {64, 128}.  No workspace.
  */
 int attn_fwd_state(const void* q, const void* k, const void* v, float* acc, float* m, float* l,
                    int B, int H, int Tq, int Tk, int d, int dv, float scale, int causal,
@@ -281,7 +281,7 @@ int attn_bwd_f32(const float* q, const float* k, const float* v, const float* o,
  *       an unknown kind or null pointers, ATTN_ERR_HIP if an event fails.
  */
 #define ATTN_KERNEL_FWD 0            /* forward main kernel */
-#define ATTN_KERNEL_FWD_AUX 1        /* forward: transposed copy of V, merge of key-split states */
+#define ATTN_KERNEL_FWD_AUX 1        /* forward: merge of key-split states (attn_fwd, attn_decode) */
 #define ATTN_KERNEL_BWD_PREP 2       /* D = rowsum(dO o O), LSE*log2(e), transposed K */
 #define ATTN_KERNEL_BWD_DKDV 3       /* backward: dK and dV */
 #define ATTN_KERNEL_BWD_DQ 4         /* backward: dQ */
