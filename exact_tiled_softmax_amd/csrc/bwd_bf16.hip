@@ -22,9 +22,6 @@
 //                  inputs that gradients flow through: "The Hidden Recurrence
 //                  in Softmax Attention", sections "Flash Attention Backward
 //                  Pass" and "Gradient at the Output"), i.e. D becomes D - dLSE.
-//   bwd_transpose  K^T ([d][Tk], Tk padded to 64 with zeros) into the
-//                  workspace, with the keys of every 16-key group in the
-//                  order the dQ MFMA operand takes them
 //   bwd_dkdv       one workgroup (8 waves) per 128 keys, walking 32-query
 //                  tiles streamed into LDS (see the kernel's comment):
 //                    S = Q K^T, dP = dO V^T, P = exp2(S*scale*log2e - LSE2),
@@ -33,7 +30,8 @@
 //                  its 32 queries' Q and dO rows as MFMA operands and dQ^T in
 //                  registers and walks 64-key tiles streamed into LDS:
 //                    S^T = K Q^T, dP^T = V dO^T, dS^T as above,
-//                    dQ^T += K^T dS^T
+//                    dQ^T += K^T dS^T (K^T fragments by transposing reads of
+//                    the row-major K tile already in LDS)
 // LDS tiles have their 16-byte chunks XOR-swizzled per row so that both
 // 16-byte row reads and transposing reads are free of bank conflicts, and
 // tiles are copied global -> LDS by the direct-to-LDS vector load, several
@@ -54,12 +52,11 @@ struct BwdArgs {
   const __bf16* v;
   const __bf16* dout;
   const float* stats;  // [BH][nqb32][64]: lse2 x32, D x32 per 32-row block
-  const __bf16* kt;    // [BH][D][Tk_pad]
   __bf16* dq;
   __bf16* dk;
   __bf16* dv;
   float* dq_part;      // [dq_splits][BH][Tq][D] fp32 when the dQ key range is split
-  int BH, Tq, Tk, Tk_pad, nqb32;
+  int BH, Tq, Tk, nqb32;
   int dq_splits, dq_tiles_per_split;  // key-range split of the dQ kernel (64-key tiles per split)
   float scale, scale_log2;
 };
@@ -386,10 +383,10 @@ struct DqCfg {
   static constexpr int CPR = D / 8;                    // 16-byte chunks per K / V row
   static constexpr int WAVES = 8;
   static constexpr int BM = 32 * WAVES;                // queries per workgroup
-  static constexpr int TILE = 64 * D;                  // bf16 elements of one K, V or K^T tile
+  static constexpr int TILE = 64 * D;                  // bf16 elements of one K or V tile
   static constexpr int DMA = TILE * 2 / 1024 / WAVES;  // wave copies per tensor and tile
-  static constexpr int VM = 3 * DMA;
-  static constexpr int STAGE = 3 * TILE;
+  static constexpr int VM = 2 * DMA;
+  static constexpr int STAGE = 2 * TILE;
   static_assert(DMA >= 1 && TILE * 2 == DMA * WAVES * 1024, "tile copy split");
 };
 
@@ -404,7 +401,6 @@ __device__ __forceinline__ void dq_issue(const BwdArgs& a, int bh, int j, __bf16
   using C = DqCfg<D>;
   const __bf16* Kh = a.k + (size_t)bh * a.Tk * D;
   const __bf16* Vh = a.v + (size_t)bh * a.Tk * D;
-  const __bf16* KTh = a.kt + (size_t)bh * D * a.Tk_pad;
 #pragma unroll
   for (int n = 0; n < C::DMA; ++n) {
     const int i = wave * C::DMA + n;
@@ -413,8 +409,6 @@ __device__ __forceinline__ void dq_issue(const BwdArgs& a, int bh, int j, __bf16
     const int kk = min(64 * j + row, a.Tk - 1);
     dma16(Kh + (size_t)kk * D + 8 * c, stg + 512 * i);
     dma16(Vh + (size_t)kk * D + 8 * c, stg + C::TILE + 512 * i);
-    const int rt = p / 8, ct = (p % 8) ^ swz<8>(rt);
-    dma16(KTh + (size_t)rt * a.Tk_pad + 64 * j + 8 * ct, stg + 2 * C::TILE + 512 * i);
   }
 }
 
@@ -443,9 +437,21 @@ __device__ __forceinline__ void dq_compute(const BwdArgs& a, DqWave& w, const __
   const int my_q = qw + lr;
   const __bf16* Ks = stg;
   const __bf16* Vs = stg + C::TILE;
-  const __bf16* KTs = stg + 2 * C::TILE;
   const int rsw = swz<C::CPR>(lr);
-  const int tsw = swz<8>(lr);
+  // K^T fragments (A operand of dQ^T += K^T dS^T: column 32cb + lane%32 of K,
+  // k-slots = the keys of dS's k-slots) by two transposing reads of the
+  // row-major K tile: rows 32u + 16s2 + 4hf + 0..3 and the same + 8
+  // (the swizzle of row r + 16k equals that of row r, so a fragment's address
+  // is a per-lane offset for its column block plus a constant for u, s2)
+  const int g16 = lane % 16, csub = (lane / 16) % 2;
+  auto at = [](int r, int cc) { return r * D + 8 * ((cc >> 3) ^ swz<C::CPR>(r)) + (cc & 7); };
+  int kofs[C::CB][2];
+#pragma unroll
+  for (int cb = 0; cb < C::CB; ++cb) {
+    const int c0 = 32 * cb + 16 * csub + 4 * (g16 % 4);
+    kofs[cb][0] = at(4 * hf + g16 / 4, c0);
+    kofs[cb][1] = at(8 + 4 * hf + g16 / 4, c0);
+  }
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int key0 = 64 * j + 32 * u;
@@ -464,8 +470,11 @@ __device__ __forceinline__ void dq_compute(const BwdArgs& a, DqWave& w, const __
 #pragma unroll
     for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-        w.dqt[cb] = mfma32(ld16(KTs + (32 * cb + lr) * 64 + 8 * ((4 * u + 2 * s2 + hf) ^ tsw)), db[s2], w.dqt[cb]);
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const __bf16* kb = Ks + (32 * u + 16 * s2) * D;
+        const bf16x8 ka = join_tr(lds_read_tr(kb + kofs[cb][0]), lds_read_tr(kb + kofs[cb][1]));
+        w.dqt[cb] = mfma32(ka, db[s2], w.dqt[cb]);
+      }
   }
 }
 
@@ -609,7 +618,7 @@ DqSplit dq_split(int BH, int Tq, int Tk) {
 }
 
 struct BwdLayout {
-  size_t stats, kt, dq_part, total;
+  size_t stats, dq_part, total;
 };
 
 BwdLayout bwd_layout(int BH, int Tq, int Tk, int d) {
@@ -619,8 +628,7 @@ BwdLayout bwd_layout(int BH, int Tq, int Tk, int d) {
   const DqSplit sp = dq_split(BH, Tq, Tk);
   BwdLayout L;
   L.stats = 0;
-  L.kt = up(L.stats + (size_t)BH * nqb32 * 64 * sizeof(float));
-  L.dq_part = up(L.kt + (size_t)BH * d * tk_pad * 2);
+  L.dq_part = up(L.stats + (size_t)BH * nqb32 * 64 * sizeof(float));
   L.total = L.dq_part + (sp.splits > 1 ? up((size_t)sp.splits * BH * Tq * d * sizeof(float)) : 0);
   return L;
 }
@@ -628,14 +636,12 @@ BwdLayout bwd_layout(int BH, int Tq, int Tk, int d) {
 template <int D>
 hipError_t bwd_launch_d(BwdArgs& args, const __bf16* o, const float* lse, const float* dlse, bool causal, char* ws,
                         const BwdLayout& L, hipStream_t stream) {
-  // pre-pass: row statistics and the transposed copy of K
+  // pre-pass: row statistics
   prof_begin(2, stream);
   {
     const int rows = args.BH * args.nqb32 * 32;
     hipLaunchKernelGGL(bwd_stats_kernel<D>, dim3((rows * 16 + 255) / 256), dim3(256), 0, stream, o, args.dout, lse,
                        dlse, reinterpret_cast<float*>(ws + L.stats), args.BH, args.Tq, args.nqb32);
-    hipLaunchKernelGGL(transpose_rows_kernel<D>, dim3(args.Tk_pad / 64, args.BH), dim3(256), 0, stream, args.k,
-                       reinterpret_cast<__bf16*>(ws + L.kt), args.Tk, args.Tk_pad);
   }
   prof_end(2, stream);
   hipError_t e = hipGetLastError();
@@ -688,14 +694,12 @@ hipError_t bwd_bf16_launch(const void* q, const void* k, const void* v, const vo
   a.v = static_cast<const __bf16*>(v);
   a.dout = static_cast<const __bf16*>(dout);
   a.stats = reinterpret_cast<const float*>(ws + L.stats);
-  a.kt = reinterpret_cast<const __bf16*>(ws + L.kt);
   a.dq = static_cast<__bf16*>(dq);
   a.dk = static_cast<__bf16*>(dk);
   a.dv = static_cast<__bf16*>(dv);
   a.BH = BH;
   a.Tq = Tq;
   a.Tk = Tk;
-  a.Tk_pad = (Tk + 63) / 64 * 64;
   a.nqb32 = (Tq + 31) / 32;
   const DqSplit sp = dq_split(BH, Tq, Tk);
   a.dq_splits = sp.splits;

@@ -45,8 +45,8 @@
  * Stream.   `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *           enqueue work on it and never synchronise; kernel faults surface at
  *           the caller's next synchronisation on that stream.
- * Workspace. Some calls need scratch memory (the transposed copy of K and
- *           row statistics of the backward, split partial states).  The library
+ * Workspace. Some calls need scratch memory (row statistics of the
+ *           backward, split partial states).  The library
  *           takes it with hipMallocAsync on `stream` and returns it with
  *           hipFreeAsync on the same stream, so its lifetime is
  *           stream-ordered and no state persists between calls.
@@ -112,9 +112,10 @@ int attn_fwd_splits(const void* q, const void* k, const void* v, void* o, float*
  * dK, dV come from one kernel that walks the queries of each key block and
  * dQ from another that walks the keys of each query block, so every output
  * element is summed in a fixed order by one workgroup: results are
- * deterministic.  Workspace (row statistics and a transposed copy of K:
- * about B*H*(Tq*8 + Tk*d*2) bytes) is allocated with hipMallocAsync on
- * `stream`.
+ * deterministic.  Workspace (row statistics, about B*H*Tq*8 bytes, and,
+ * when the dQ kernel splits the key range because there are few query
+ * blocks, fp32 partial dQ of splits*B*H*Tq*d*4 bytes) is allocated with
+ * hipMallocAsync on `stream`.
  * Supported: d == dv, d in {64, 128}; otherwise ATTN_ERR_UNSUPPORTED.
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -282,7 +283,7 @@ int attn_bwd_f32(const float* q, const float* k, const float* v, const float* o,
  */
 #define ATTN_KERNEL_FWD 0            /* forward main kernel */
 #define ATTN_KERNEL_FWD_AUX 1        /* forward: merge of key-split states (attn_fwd, attn_decode) */
-#define ATTN_KERNEL_BWD_PREP 2       /* D = rowsum(dO o O), LSE*log2(e), transposed K */
+#define ATTN_KERNEL_BWD_PREP 2       /* D = rowsum(dO o O) (- dLSE), LSE*log2(e) */
 #define ATTN_KERNEL_BWD_DKDV 3       /* backward: dK and dV */
 #define ATTN_KERNEL_BWD_DQ 4         /* backward: dQ */
 #define ATTN_KERNEL_DECODE 5         /* decode main kernel (its split merge counts as ATTN_KERNEL_FWD_AUX) */
