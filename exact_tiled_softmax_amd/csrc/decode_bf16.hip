@@ -328,6 +328,7 @@ int decode_bf16_num_splits(int BH, int Tk, int d, int requested) {
   }
   if (s > max_splits) s = max_splits;
   if (s > kDecodeMaxSplits) s = kDecodeMaxSplits;
+  if ((long long)s * BH > 2147483647LL) s = (int)(2147483647LL / BH);  // workgroup count fits an int
   if (s < 1) s = 1;
   return s;
 }

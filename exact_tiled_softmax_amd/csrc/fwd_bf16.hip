@@ -383,6 +383,9 @@ int fwd_bf16_num_splits(int BH, int Tq, int Tk, int causal, int requested) {
     }
   }
   if (s > kblocks) s = kblocks;
+  // the workgroup count BH * qtiles * s must fit an int
+  const long long cap = 2147483647LL / ((long long)BH * qtiles);
+  if (s > cap) s = (int)cap;
   if (s < 1) s = 1;
   return s;
 }
