@@ -194,6 +194,71 @@ def test_bf16_bwd_long_keys_split_dq(dev, shape, causal):
     assert torch.equal(dq.view(torch.int16), dq2.view(torch.int16))  # fixed summation order
 
 
+# Seeded random shapes: ragged query and key counts on both sides of every
+# tile size, both head dims, both masks, Tq above and below Tk.
+def _random_shape(seed):
+    g = np.random.default_rng(seed)
+    d = int(g.choice([64, 128]))
+    return (int(g.integers(1, 3)), int(g.integers(1, 4)), int(g.integers(1, 600)), int(g.integers(1, 600)), d, d), \
+        bool(g.integers(0, 2))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_bf16_random_shapes_fwd_bwd(dev, seed):
+    shape, causal = _random_shape(seed)
+    q, k, v, do = bf16_problem(shape, seed=100 + seed)
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    o, lse = attn.fwd(qd, kd, vd, causal=causal)
+    dq, dk, dv = attn.bwd(qd, kd, vd, o, lse, dod, causal=causal)
+    torch.cuda.synchronize()
+    scale = 1 / np.sqrt(shape[4])
+    ro, rl = dense_forward(f64(q), f64(k), f64(v), scale, causal)
+    assert_close(f"O {shape} causal={causal}", f64(o), ro, TOL_BF16)
+    assert_close("LSE", f64(lse), rl, TOL_LSE_BF16)
+    rq, rk, rv = dense_backward(f64(q), f64(k), f64(v), f64(do), scale, causal)
+    assert_close("dQ", f64(dq), rq, TOL_BF16)
+    assert_close("dK", f64(dk), rk, TOL_BF16)
+    assert_close("dV", f64(dv), rv, TOL_BF16)
+
+
+# Large scores from bf16 inputs: queries scaled so that scores reach about
+# +-100 (forward) and +-12 (backward), so the running maximum moves by many
+# units across key tiles.  The backward stays moderate and non-causal: on a
+# near one-hot row the exact dS = P (dP - D) cancels to zero, while D is
+# formed from the forward's bf16-rounded O (the backward takes O as given),
+# which leaves an error of order |dO| |O| 2^-8 times scale |K| in dQ; the
+# first rows of a causal mask, with only a few keys, are near one-hot at
+# this scale.  The causal backward is covered at unit scale above.
+@pytest.mark.parametrize("sigma_q", [8.0, 30.0])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_fwd_large_scores(dev, sigma_q, causal):
+    shape = (1, 2, 300, 900, 128, 128)
+    q, k, v, _ = bf16_problem(shape, seed=11, sigma_q=sigma_q)
+    o, lse = attn.fwd(q.to(dev), k.to(dev), v.to(dev), causal=causal)
+    torch.cuda.synchronize()
+    ro, rl = dense_forward(f64(q), f64(k), f64(v), 1 / np.sqrt(128), causal)
+    assert np.all(np.isfinite(f64(o))) and np.all(np.isfinite(f64(lse)))
+    assert_close("O", f64(o), ro, TOL_BF16)
+    assert_close("LSE", f64(lse), rl, TOL_LSE_BF16)
+
+
+def test_bf16_bwd_moderately_large_scores(dev):
+    causal = False
+    sigma_q = 4.0
+    shape = (1, 2, 300, 700, 128, 128)
+    q, k, v, do = bf16_problem(shape, seed=12, sigma_q=sigma_q)
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    o, lse = attn.fwd(qd, kd, vd, causal=causal)
+    dq, dk, dv = attn.bwd(qd, kd, vd, o, lse, dod, causal=causal)
+    torch.cuda.synchronize()
+    rq, rk, rv = dense_backward(f64(q), f64(k), f64(v), f64(do), 1 / np.sqrt(128), causal)
+    assert_close("dQ", f64(dq), rq, TOL_BF16)
+    # dK = scale * dS^T Q is linear in Q: its rounding error grows with |Q|, and
+    # the bf16 bound is stated for unit-variance inputs, so it scales by sigma_q
+    assert_close("dK", f64(dk), rk, TOL_BF16 * sigma_q)
+    assert_close("dV", f64(dv), rv, TOL_BF16)
+
+
 def test_bf16_inputs_unchanged_and_results_deterministic(dev):
     q, k, v, do = bf16_problem((1, 2, 300, 333, 128, 128), seed=9)
     qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
