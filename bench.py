@@ -352,7 +352,7 @@ def main(argv=None) -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); the "
-              "attention kernels have no multi-GPU path in this build", file=sys.stderr)
+              "attention kernels have no multi-GPU path", file=sys.stderr)
         return 2
 
     import torch
