@@ -456,25 +456,43 @@ __device__ __forceinline__ void dq_compute(const BwdArgs& a, DqWave& w, const __
   for (int u = 0; u < 2; ++u) {
     const int key0 = 64 * j + 32 * u;
     if (key0 >= kend) break;
-    // the S^T and dP^T chains alternate
+    // K and V fragments four k-steps ahead of their MFMAs (each read issued
+    // after the MFMA that frees its registers); the S^T and dP^T chains
+    // alternate
+    constexpr int LA = C::KS < 4 ? C::KS : 4;
+    bf16x8 kfr[C::KS], vfr[C::KS];
+    auto rd = [&](int ks) {
+      const int off = (32 * u + lr) * D + 8 * ((2 * ks + hf) ^ rsw);
+      kfr[ks] = ld16(Ks + off);
+      vfr[ks] = ld16(Vs + off);
+    };
+#pragma unroll
+    for (int ks = 0; ks < LA; ++ks) rd(ks);
     f32x16 st = {}, dpt = {};
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-      const int off = (32 * u + lr) * D + 8 * ((2 * ks + hf) ^ rsw);
-      st = mfma32(ld16(Ks + off), w.qf[ks], st);
-      dpt = mfma32(ld16(Vs + off), w.df[ks], dpt);
+      __builtin_amdgcn_sched_barrier(0);
+      st = mfma32(kfr[ks], w.qf[ks], st);
+      dpt = mfma32(vfr[ks], w.df[ks], dpt);
+      if (ks + LA < C::KS) rd(ks + LA);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    // K^T fragments read while the softmax runs
+    bf16x8 ka[C::CB][2];
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const __bf16* kb = Ks + (32 * u + 16 * s2) * D;
+        ka[cb][s2] = join_tr(lds_read_tr(kb + kofs[cb][0]), lds_read_tr(kb + kofs[cb][1]));
+      }
     bf16x8 db[2];
     if ((CAUSAL && key0 + 31 > qw) || key0 + 32 > a.Tk) dq_softmax<CAUSAL, true>(a, w, st, dpt, key0, my_q, hf, db);
     else dq_softmax<CAUSAL, false>(a, w, st, dpt, key0, my_q, hf, db);
 #pragma unroll
     for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const __bf16* kb = Ks + (32 * u + 16 * s2) * D;
-        const bf16x8 ka = join_tr(lds_read_tr(kb + kofs[cb][0]), lds_read_tr(kb + kofs[cb][1]));
-        w.dqt[cb] = mfma32(ka, db[s2], w.dqt[cb]);
-      }
+      for (int s2 = 0; s2 < 2; ++s2) w.dqt[cb] = mfma32(ka[cb][s2], db[s2], w.dqt[cb]);
   }
 }
 
