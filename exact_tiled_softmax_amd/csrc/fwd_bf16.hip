@@ -116,13 +116,26 @@ __device__ __forceinline__ void fwd_tile(const __bf16* stg, const bf16x8 (&qf)[8
   const __bf16* Ks = stg;
   const __bf16* Vs = stg + C::TILE;
   const int rsw = swz<C::CPR>(lr);
-  // the two 32-key score chains alternate
+  // the two 32-key score chains alternate; K fragments are read 4 k-steps
+  // ahead of their MFMAs (each read issued after the MFMA that frees its
+  // registers)
+  constexpr int LA = C::KS < 4 ? C::KS : 4;
+  bf16x8 kfr[C::KS][2];
+  auto rd = [&](int ks) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) kfr[ks][u] = ld16(Ks + (32 * u + lr) * D + 8 * ((2 * ks + hf) ^ rsw));
+  };
+#pragma unroll
+  for (int ks = 0; ks < LA; ++ks) rd(ks);
   f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks)
+  for (int ks = 0; ks < C::KS; ++ks) {
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-      s[u] = mfma32(ld16(Ks + (32 * u + lr) * D + 8 * ((2 * ks + hf) ^ rsw)), qf[ks], s[u]);
+    for (int u = 0; u < 2; ++u) s[u] = mfma32(kfr[ks][u], qf[ks], s[u]);
+    if (ks + LA < C::KS) rd(ks + LA);
+  }
+  __builtin_amdgcn_sched_barrier(0);
 
   // accumulator register r of block u: key key0 + 32u + 8(r/4) + 4hf + r%4
   float cc = c;
