@@ -68,6 +68,9 @@ WORKLOADS = {
         # decode: one new query per sequence against a 32768-slot cache, 8
         # sequences of mixed lengths (kv_lens), 32 heads
         Workload("decode_bf16_b8h32_tk32768_d128", 6, 8, 32, 1, 32768, 128, 128, True, "bf16", decode=True),
+        # index range: K and V hold 128 * 131072 * 128 = 2^31 elements each, so
+        # element offsets of the last heads pass the int32 range
+        Workload("index_bf16_b1h128_tq128_tk131072_d128", 7, 1, 128, 128, 131072, 128, 128, False, "bf16"),
     ]
 }
 

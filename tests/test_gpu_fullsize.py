@@ -111,3 +111,4 @@ def test_longkv_tq256_tk65536(dev):
     t, o, lse, grads = run_workload(w, dev, with_bwd=True)
     check_properties(t, o, lse, grads)
     check_heads(w, o, lse, grads, [(0, 0), (0, 63)], 400)
+
