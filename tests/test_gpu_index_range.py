@@ -1,5 +1,4 @@
-"""GPU parity with more than 2^31 elements in one tensor (not collected by
-pytest until it has run on a GPU; run it by naming this file).
+"""GPU parity with more than 2^31 elements in one tensor.
 
 K, V, dK and dV of the index-range workload hold 2^31 elements each, so any
 32-bit element offset in the kernels would wrap on the last heads.
