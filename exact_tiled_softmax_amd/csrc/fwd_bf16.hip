@@ -64,6 +64,7 @@ struct FwdCfg {
   static constexpr int AHEAD = NSTAGE - 1;               // tiles in flight ahead of the compute
   static constexpr int WG_PER_CU = 1;
   static_assert(PER_WAVE >= 1 && 2 * PER_TENSOR == PER_WAVE * WAVES, "tile copy split");
+  static_assert(PER_TENSOR % PER_WAVE == 0, "the copies of one wave belong to one tensor");
 };
 
 struct FwdArgs {
@@ -218,6 +219,29 @@ __global__ __launch_bounds__(FwdCfg<D>::THREADS, FwdCfg<D>::WG_PER_CU) void fwd_
   const int q0 = qt * C::BM;
   const int row = q0 + wave * 32 + lr;  // this lane's query row
   const __bf16* Qh = a.q + (size_t)bh * a.Tq * D;
+  // Tile copies: a tile that lies inside [0, Tk) is copied from a
+  // wave-uniform base with per-lane byte offsets computed here once (the
+  // layout of fwd_issue); a tile that runs past Tk clamps its rows per lane.
+  uint32_t voff[C::PER_WAVE];
+#pragma unroll
+  for (int n = 0; n < C::PER_WAVE; ++n) {
+    const int i = (wave * C::PER_WAVE + n) % C::PER_TENSOR, p = 64 * i + lane;
+    const int rr = p / C::CPR, cc = (p % C::CPR) ^ swz<C::CPR>(rr);
+    voff[n] = (uint32_t)((rr * D + 8 * cc) * (int)sizeof(__bf16));
+  }
+  auto issue = [&](int key0, __bf16* stg) {
+    if (key0 + C::BN <= a.Tk) {
+      const int tensor = (wave * C::PER_WAVE) / C::PER_TENSOR;  // the same for all copies of a wave
+      const __bf16* base = (tensor == 0 ? a.k : a.v) + ((size_t)bh * a.Tk + key0) * D;
+#pragma unroll
+      for (int n = 0; n < C::PER_WAVE; ++n) {
+        const int i = (wave * C::PER_WAVE + n) % C::PER_TENSOR;
+        dma16_sbase(base, voff[n], stg + tensor * C::TILE + 512 * i);
+      }
+    } else {
+      fwd_issue<D>(a, bh, key0, stg, wave, lane);
+    }
+  };
 
   int kbeg = 0, kend = a.Tk;
   if (SPLIT) {
@@ -249,7 +273,7 @@ __global__ __launch_bounds__(FwdCfg<D>::THREADS, FwdCfg<D>::WG_PER_CU) void fwd_
   const float c = a.scale_log2;
 
   auto stage = [&](int t) { return stages + (t % C::NSTAGE) * C::STAGE; };
-  for (int t = 0; t < C::AHEAD && t < ntiles; ++t) fwd_issue<D>(a, bh, kbeg + t * C::BN, stage(t), wave, lane);
+  for (int t = 0; t < C::AHEAD && t < ntiles; ++t) issue(kbeg + t * C::BN, stage(t));
   static_assert(C::AHEAD >= 1 && C::AHEAD <= 3, "the waits below cover up to 2 later tiles");
   for (int t = 0; t < ntiles; ++t) {
     // this wave's copies of tiles t+1 .. t+AHEAD-1 may still be in flight
@@ -258,7 +282,7 @@ __global__ __launch_bounds__(FwdCfg<D>::THREADS, FwdCfg<D>::WG_PER_CU) void fwd_
     else if (C::AHEAD >= 2 && later == 1) wait_vm<C::VM>();
     else wait_vm<0>();
     barrier();
-    if (t + C::AHEAD < ntiles) fwd_issue<D>(a, bh, kbeg + (t + C::AHEAD) * C::BN, stage(t + C::AHEAD), wave, lane);
+    if (t + C::AHEAD < ntiles) issue(kbeg + (t + C::AHEAD) * C::BN, stage(t + C::AHEAD));
     const int key0 = kbeg + t * C::BN;
     if (key0 < wave_kend) {
       const bool need_mask = (key0 + C::BN > kend) || (CAUSAL && key0 + C::BN - 1 > wave_row0 + a.diag);

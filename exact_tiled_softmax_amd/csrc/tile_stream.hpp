@@ -27,6 +27,17 @@ __device__ __forceinline__ void dma16(const __bf16* src, const __bf16* lds_base)
 #pragma clang diagnostic pop
 }
 
+// The same copy from a wave-uniform 64-bit base in SGPRs plus a 32-bit
+// per-lane byte offset: no per-lane address arithmetic per copy.
+__device__ __forceinline__ void dma16_sbase(const void* sbase, uint32_t voff, const __bf16* lds_base) {
+  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_cvoid*)lds_base));
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
+               : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
 // Wait until at most N vector-memory operations of this wave are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
