@@ -339,6 +339,9 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle work (0 = skip)")
+    ap.add_argument("--flush-mib", type=int, default=0, metavar="MIB",
+                    help="write this many MiB before every step (evicts L2 and the Infinity Cache); the step time "
+                         "is then the attention kernels' own event time, without the flush")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the reference kernel "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes) and exit")
@@ -386,7 +389,11 @@ def main(argv=None) -> int:
     lse = torch.empty((w.B, w.H, w.Tq), dtype=torch.float32, device=dev)
     dq, dk, dvg = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
 
+    flush = torch.empty(args.flush_mib << 18, dtype=torch.float32, device=dev) if args.flush_mib > 0 else None
+
     def step():
+        if flush is not None:
+            flush.fill_(1.0)
         attn.fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse)
         attn.bwd(q, k, v, o, lse, do, scale=w.scale, causal=w.causal, dq=dq, dk=dk, dv=dvg)
 
@@ -407,9 +414,11 @@ def main(argv=None) -> int:
 
     pairs, fwd_fl, bwd_fl, fwd_b, bwd_b = work(w)
     ms_step = (t1 - t0) * 1e3 / args.steps
-    total_tflops = (fwd_fl + bwd_fl) / (ms_step * 1e-3) / 1e12
     fwd_ms = (kern["fwd"][0] + kern["fwd_aux"][0]) / args.steps
     bwd_ms = (kern["bwd_prep"][0] + kern["bwd_dkdv"][0] + kern["bwd_dq"][0]) / args.steps
+    if flush is not None:
+        ms_step = fwd_ms + bwd_ms  # the flush between steps is not attention work
+    total_tflops = (fwd_fl + bwd_fl) / (ms_step * 1e-3) / 1e12
     fwd_tflops = fwd_fl / (fwd_ms * 1e-3) / 1e12 if fwd_ms > 0 else None
     bwd_tflops = bwd_fl / (bwd_ms * 1e-3) / 1e12 if bwd_ms > 0 else None
 
@@ -455,7 +464,8 @@ def main(argv=None) -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Tq": w.Tq, "Tk": w.Tk, "d": w.d, "dv": w.dv,
-                   "causal": w.causal, "step": "attn_fwd + attn_bwd"},
+                   "causal": w.causal, "step": "attn_fwd + attn_bwd",
+                   **({"flush_mib_between_steps": args.flush_mib} if flush is not None else {})},
         "fwd_tflops": round(fwd_tflops, 2) if fwd_tflops else None,
         "fwd_frac_of_peak": round(fwd_tflops / PEAK_BF16_TFLOPS, 4) if fwd_tflops else None,
         "bwd_tflops": round(bwd_tflops, 2) if bwd_tflops else None,
