@@ -91,4 +91,24 @@ __device__ __forceinline__ int xcd_remap(int wg, int n) {
   return (x < rem) ? x * (per + 1) + slot : rem * (per + 1) + (x - rem) * per + slot;
 }
 
+// Work item of a launch over (head, block, split), block 0 the heaviest: the
+// logical items of each group of G consecutive heads are ordered block-major
+// (block, then head, then split), so that a group's heaviest blocks of all
+// its heads are dispatched before any of their lighter ones.  G = 1 is
+// head-major.  With xcd_remap, a group whose items fill one XCD's range
+// keeps its heads on that XCD.
+struct WorkItem {
+  int bh, blk, split;
+};
+__device__ __forceinline__ WorkItem work_item(int item, int BH, int nblk, int nsplit, int G) {
+  const int full = G * nblk * nsplit;
+  const int g = item / full, r = item % full;
+  const int gsize = min(G, BH - g * G);
+  WorkItem w;
+  w.blk = r / (gsize * nsplit);
+  w.bh = g * G + (r / nsplit) % gsize;
+  w.split = r % nsplit;
+  return w;
+}
+
 }  // namespace attn

@@ -13,6 +13,21 @@ namespace attn {
 void prof_begin(int kind, hipStream_t stream);
 void prof_end(int kind, hipStream_t stream);
 
+// Heads whose blocks a launch dispatches interleaved (work_item).  With fewer
+// than eight workgroups per CU, a head-major order leaves the heavy causal
+// blocks of an XCD's last head to run after the light blocks of its first
+// ones (at B=2, H=16, L=4096 the dQ and forward launches finish at about 1.5x
+// their balanced time), so the BH / 8 heads that one XCD holds are
+// interleaved block-major instead.  Only when BH is a multiple of 8, so that
+// each group fills exactly one XCD's range of xcd_remap; with more
+// workgroups per CU the head-major order keeps one head per XCD (its K/V
+// stay in that XCD's L2) and already balances.
+inline int head_group(int BH, int items_per_head) {
+  const long long items = (long long)BH * items_per_head;
+  if (items >= 8LL * 256 || BH % 8 != 0 || BH < 16) return 1;
+  return BH / 8;
+}
+
 // ---- bf16 forward ---------------------------------------------------------------
 // Number of key splits to use (requested <= 0: heuristic), clamped to the number
 // of 64-key blocks.

@@ -58,6 +58,7 @@ struct BwdArgs {
   float* dq_part;      // [dq_splits][BH][Tq][D] fp32 when the dQ key range is split
   int BH, Tq, Tk, nqb32;
   int dq_splits, dq_tiles_per_split;  // key-range split of the dQ kernel (64-key tiles per split)
+  int dq_head_group;                  // heads whose query blocks the dQ kernel dispatches interleaved
   float scale, scale_log2;
 };
 
@@ -512,11 +513,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a) {
   const int lr = lane % 32, hf = lane / 32;
   const int nqb = (a.Tq + C::BM - 1) / C::BM;
   const int ns = SPLIT ? a.dq_splits : 1;
-  const int item = xcd_remap(blockIdx.x, a.BH * nqb * ns);
-  const int split = item % ns;
-  const int bh = item / (nqb * ns);
-  const int qi = (item / ns) % nqb;
-  const int qb = CAUSAL ? nqb - 1 - qi : qi;  // most causal work first within a head
+  const WorkItem wi = work_item(xcd_remap(blockIdx.x, a.BH * nqb * ns), a.BH, nqb, ns, a.dq_head_group);
+  const int split = wi.split;
+  const int bh = wi.bh;
+  const int qi = wi.blk;
+  const int qb = CAUSAL ? nqb - 1 - qi : qi;  // most causal work first
   const int q0 = qb * C::BM;
   const int qw = q0 + 32 * wave;
   const int my_q = qw + lr;
@@ -721,6 +722,7 @@ hipError_t bwd_bf16_launch(const void* q, const void* k, const void* v, const vo
   a.nqb32 = (Tq + 31) / 32;
   const DqSplit sp = dq_split(BH, Tq, Tk);
   a.dq_splits = sp.splits;
+  a.dq_head_group = head_group(BH, ((Tq + DqCfg<128>::BM - 1) / DqCfg<128>::BM) * sp.splits);
   a.dq_tiles_per_split = sp.tiles_per_split;
   a.dq_part = sp.splits > 1 ? reinterpret_cast<float*>(ws + L.dq_part) : nullptr;
   a.scale = scale;

@@ -79,6 +79,7 @@ struct FwdArgs {
   int BH, Tq, Tk, Tk_pad;
   int diag;          // causal: key j is blocked for query i when j > i + diag
   int num_qtiles, num_splits, keys_per_split;
+  int head_group;    // heads whose query tiles are dispatched interleaved (work_item)
   float scale_log2;  // scale * log2(e)
 };
 
@@ -209,12 +210,11 @@ __global__ __launch_bounds__(FwdCfg<D>::THREADS, FwdCfg<D>::WG_PER_CU) void fwd_
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   const int lr = lane % 32, hf = lane / 32;
   const int n_items = a.BH * a.num_qtiles * a.num_splits;
-  const int item = xcd_remap(blockIdx.x, n_items);
-  // item = (bh * num_qtiles + (num_qtiles-1-qt)) * num_splits + split: heads
-  // outermost, heavier (later) causal query tiles first within a head.
-  const int split = item % a.num_splits;
-  const int qt = a.num_qtiles - 1 - (item / a.num_splits) % a.num_qtiles;
-  const int bh = item / (a.num_splits * a.num_qtiles);
+  // heavier (later) causal query tiles first
+  const WorkItem wi = work_item(xcd_remap(blockIdx.x, n_items), a.BH, a.num_qtiles, a.num_splits, a.head_group);
+  const int split = wi.split;
+  const int qt = a.num_qtiles - 1 - wi.blk;
+  const int bh = wi.bh;
 
   const int q0 = qt * C::BM;
   const int row = q0 + wave * 32 + lr;  // this lane's query row
@@ -451,6 +451,7 @@ FwdArgs fwd_args(const void* q, const void* k, const void* v, void* o, float* ls
   args.num_splits = num_splits;
   const int kblocks = (Tk + kBN - 1) / kBN;
   args.keys_per_split = ((kblocks + num_splits - 1) / num_splits) * kBN;
+  args.head_group = head_group(BH, args.num_qtiles * num_splits);
   args.scale_log2 = scale * kLog2e;
   return args;
 }
