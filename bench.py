@@ -39,6 +39,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 HEADLINE = "causal_bf16_b2h32_t8192_d128"
+BWD_TARGET = "bwd_causal_bf16_b2h16_t4096_d128"  # the causal backward workload reported beside it
 METRIC = "attention TFLOP/s fwd & fwd+bwd, bf16 d=128 L=8192 causal; % of MFMA peak"
 
 
@@ -75,6 +76,22 @@ def work(w):
     return pairs, fwd, bwd, fwd_bytes, bwd_bytes
 
 
+def kernel_bytes(w):
+    """Algorithmic HBM bytes per launch of each kernel: what it must read
+    (every input once) and write (every output once).  Row statistics of the
+    backward are 8 bytes per query row (LSE and D, fp32)."""
+    e = 2  # bf16 bytes
+    bh = w.B * w.H
+    qo = e * (w.Tq * w.d + w.Tq * w.dv)  # Q and dO (or Q and O)
+    kv = e * (w.Tk * w.d + w.Tk * w.dv)  # K and V
+    return {
+        "fwd": bh * (qo + kv + 4 * w.Tq),
+        "bwd_prep": bh * (2 * e * w.Tq * w.dv + 4 * w.Tq + 8 * w.Tq),
+        "bwd_dkdv": bh * (qo + kv + 8 * w.Tq + kv),
+        "bwd_dq": bh * (qo + kv + 8 * w.Tq + e * w.Tq * w.d),
+    }
+
+
 def kernel_source_digest(files):
     h = hashlib.sha256()
     for f in files:
@@ -104,42 +121,69 @@ def measured_traffic(kernel: str, workload: str):
     return float(m_b.group(1))
 
 
-def cpu_baseline(w, budget_s: float):
-    """The float64 oracle (dense forward + backward) on whole heads of the
-    workload, as many heads as fit in about `budget_s` seconds (at least one)."""
+def host_workers() -> int:
+    """Worker processes for the CPU oracle: the cores this process may run on,
+    capped by OMP_NUM_THREADS when it is set (the host's share of CPUs)."""
+    n = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS")
+    if cap and cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
+def _oracle_head(args):
+    """One pool task: the float64 oracle's dense forward + backward of one
+    head, with single-threaded BLAS; returns (start, end) of the oracle call
+    on the shared monotonic clock."""
+    w, b, h = args
+    from threadpoolctl import threadpool_limits
+
     import numpy as np
-    from threadpoolctl import threadpool_info
 
     from exact_tiled_softmax_amd.inputs import make_head
     from oracle import dense_backward, dense_forward
 
-    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
-    done = []
-    flops = 0
-    elapsed = 0.0
-    per_head_pairs = unmasked_pairs(w.Tq, w.Tk, w.causal)
-    for b, h in heads:
-        q, k, v, do = (make_head(w, n, b, h) for n in ("q", "k", "v", "do"))
+    q, k, v, do = (make_head(w, n, b, h) for n in ("q", "k", "v", "do"))
+    with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        o, lse = dense_forward(q, k, v, w.scale, w.causal)
-        dq, dk, dv = dense_backward(q, k, v, do, w.scale, w.causal)
-        elapsed += time.perf_counter() - t0
-        assert np.isfinite(o).all() and np.isfinite(dq).all()
-        done.append((b, h))
-        flops += 2 * per_head_pairs * ((w.d + w.dv) + (3 * w.d + 2 * w.dv))
-        if elapsed >= budget_s:
-            break
-    threads = 1
-    for info in threadpool_info():
-        if info.get("user_api") == "blas":
-            threads = max(threads, int(info.get("num_threads", 1)))
+        o, _ = dense_forward(q, k, v, w.scale, w.causal)
+        dq, _, _ = dense_backward(q, k, v, do, w.scale, w.causal)
+        t1 = time.perf_counter()
+    assert np.isfinite(o).all() and np.isfinite(dq).all()
+    return t0, t1
+
+
+def cpu_baseline(w, budget_s: float):
+    """The float64 oracle (dense forward + backward) on whole heads of the
+    workload: a pool of single-threaded workers, one per host core, each
+    taking one head at a time; as many rounds of heads as fit in about
+    `budget_s` seconds (at least one).  Must run before the process touches
+    the GPU (the pool forks)."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+
+    workers = host_workers()
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    per_head_flops = 2 * unmasked_pairs(w.Tq, w.Tk, w.causal) * ((w.d + w.dv) + (3 * w.d + 2 * w.dv))
+    done, spans = 0, []
+    t_begin = time.perf_counter()
+    with ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("fork")) as ex:
+        while done < len(heads):
+            batch = heads[done:done + workers]
+            spans += list(ex.map(_oracle_head, [(w, b, h) for b, h in batch]))
+            done += len(batch)
+            if time.perf_counter() - t_begin >= budget_s:
+                break
+    wall = max(e for _, e in spans) - min(s for s, _ in spans)
     return {
-        "value": flops / elapsed / 1e12,
+        "value": done * per_head_flops / wall / 1e12,
         "unit": "TFLOP/s",
-        "cores": threads,
+        "cores": workers,
+        "blas_threads_per_core": 1,
         "kind": "oracle",
-        "sample": (f"{len(done)} of {w.B * w.H} heads of {w.name} (first: b,h={done[0]}), forward+backward in "
-                   f"float64 numpy with full score rows, {elapsed:.1f} s; same algorithmic flop count as the GPU"),
+        "sample": (f"{done} of {w.B * w.H} heads of {w.name} (first: b,h={heads[0]}), forward+backward in float64 "
+                   f"numpy with full score rows, one head per worker process, {workers} single-threaded workers, "
+                   f"{wall:.1f} s wall; same algorithmic flop count as the GPU"),
     }
 
 
@@ -154,9 +198,9 @@ def decode_bytes(w, lens):
 def cpu_baseline_decode(w, lens, budget_s: float):
     """The float64 oracle decode over the whole workload (every sequence, all
     heads), repeated until about `budget_s` seconds of oracle time have run
-    (one pass takes well under a second)."""
+    (one pass takes well under a second); one process, single-threaded BLAS."""
     import numpy as np
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_limits
 
     from exact_tiled_softmax_amd.inputs import make_head
     from oracle import decode_forward
@@ -169,29 +213,27 @@ def cpu_baseline_decode(w, lens, budget_s: float):
         v = np.stack([make_head(w, "v", b, h)[:n] for h in range(w.H)])[None]
         seqs.append((n, q, k, v))
     passes, elapsed = 0, 0.0
-    while passes == 0 or elapsed < budget_s:
-        for n, q, k, v in seqs:
-            t0 = time.perf_counter()
-            o, lse = decode_forward(q, k, v, w.scale, kv_lens=[n], causal=w.causal)
-            elapsed += time.perf_counter() - t0
-            assert np.isfinite(o).all()
-        passes += 1
-    threads = 1
-    for info in threadpool_info():
-        if info.get("user_api") == "blas":
-            threads = max(threads, int(info.get("num_threads", 1)))
+    with threadpool_limits(limits=1):
+        while passes == 0 or elapsed < budget_s:
+            for n, q, k, v in seqs:
+                t0 = time.perf_counter()
+                o, lse = decode_forward(q, k, v, w.scale, kv_lens=[n], causal=w.causal)
+                elapsed += time.perf_counter() - t0
+                assert np.isfinite(o).all()
+            passes += 1
     return {
         "value": passes * decode_bytes(w, lens) / elapsed / 1e9,
         "unit": "GB/s",
-        "cores": threads,
+        "cores": 1,
+        "blas_threads_per_core": 1,
         "kind": "oracle",
         "sample": (f"the whole workload {w.name} ({w.B} sequences x {w.H} heads, cache lengths "
-                   f"{[int(x) for x in lens]}) {passes} times, float64 numpy, {elapsed:.1f} s; same algorithmic "
-                   f"byte count as the GPU"),
+                   f"{[int(x) for x in lens]}) {passes} times, float64 numpy in one single-threaded process, "
+                   f"{elapsed:.1f} s; same algorithmic byte count as the GPU"),
     }
 
 
-def bench_decode(args, w) -> int:
+def bench_decode(args, w, cpu) -> int:
     import torch
 
     from exact_tiled_softmax_amd import attn
@@ -240,10 +282,6 @@ def bench_decode(args, w) -> int:
         "launches": kern["decode"][1],
         "algorithmic_bytes_per_launch": nbytes,
     }
-    cpu = None
-    if args.cpu_budget > 0:
-        print(f"[bench] timing the CPU oracle (~{args.cpu_budget:.0f} s)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline_decode(w, lens_np, args.cpu_budget)
     line = {
         "metric": "decode HBM GB/s (algorithmic bytes), bf16 d=128, 1 query against a mixed-length KV cache",
         "value": round(gbs, 1),
@@ -332,6 +370,49 @@ def bench_standard(args, w) -> int:
     return 0
 
 
+def time_steps(attn, w, dev, steps, warmup, flush_mib=0):
+    """Warm up, then time `steps` fwd+bwd steps of workload w with inputs
+    resident on `dev`.  Returns ({kernel: (total_ms, launches)} from the
+    library's HIP events, wall ms per step).  With flush_mib > 0 a buffer of
+    that size is written before every step and the step time is the
+    attention kernels' own event time."""
+    import torch
+
+    from exact_tiled_softmax_amd.inputs import make_tensor
+
+    print(f"[bench] building inputs for {w.name}", file=sys.stderr, flush=True)
+    q, k, v, do = (make_tensor(w, n).to(dev) for n in ("q", "k", "v", "do"))
+    o = torch.empty((w.B, w.H, w.Tq, w.dv), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.H, w.Tq), dtype=torch.float32, device=dev)
+    dq, dk, dvg = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    flush = torch.empty(flush_mib << 18, dtype=torch.float32, device=dev) if flush_mib > 0 else None
+
+    def step():
+        if flush is not None:
+            flush.fill_(1.0)
+        attn.fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse)
+        attn.bwd(q, k, v, o, lse, do, scale=w.scale, causal=w.causal, dq=dq, dk=dk, dv=dvg)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] {w.name}: warmup done ({warmup} steps); timing {steps} steps", file=sys.stderr, flush=True)
+    attn.profile_start()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    attn.profile_stop()
+    kern = {name: attn.profile_query(kind) for kind, name in attn.KERNEL_NAMES.items()}
+    ms_step = (t1 - t0) * 1e3 / steps
+    if flush is not None:
+        # the flush between steps is not attention work
+        ms_step = sum(kern[n][0] for n in ("fwd", "fwd_aux", "bwd_prep", "bwd_dkdv", "bwd_dq")) / steps
+    return kern, ms_step
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -350,6 +431,8 @@ def main(argv=None) -> int:
                          "workload and print the IO comparison line instead of the fwd+bwd step")
     ap.add_argument("--decode-splits", type=int, default=0,
                     help="decode workloads: key-range splits per sequence (0 = the library's choice)")
+    ap.add_argument("--no-targets", dest="targets", action="store_false",
+                    help="headline workload only: skip timing the L=4096 causal backward workload in the same run")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -361,7 +444,15 @@ def main(argv=None) -> int:
     import torch
 
     from exact_tiled_softmax_amd import attn
-    from exact_tiled_softmax_amd.inputs import WORKLOADS, make_tensor
+    from exact_tiled_softmax_amd.inputs import WORKLOADS, kv_lens
+
+    w = WORKLOADS[args.workload]
+    # The CPU oracle runs first: its worker pool forks, which must happen
+    # before this process initialises the GPU.
+    cpu = None
+    if args.cpu_budget > 0 and not args.copy_calibration and not args.standard and w.dtype == "bf16":
+        print(f"[bench] timing the CPU oracle (~{args.cpu_budget:.0f} s)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline_decode(w, kv_lens(w), args.cpu_budget) if w.decode else cpu_baseline(w, args.cpu_budget)
 
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     if args.copy_calibration:
@@ -374,56 +465,25 @@ def main(argv=None) -> int:
         print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "launches": 3}))
         return 0
     attn.load()
-    w = WORKLOADS[args.workload]
     if w.dtype != "bf16":
         print("bench.py times the bf16 path", file=sys.stderr)
         return 2
     if w.decode:
-        return bench_decode(args, w)
+        return bench_decode(args, w, cpu)
     if args.standard:
         return bench_standard(args, w)
     dev = torch.device("cuda:0")
-    print(f"[bench] building inputs for {w.name}", file=sys.stderr, flush=True)
-    q, k, v, do = (make_tensor(w, n).to(dev) for n in ("q", "k", "v", "do"))
-    o = torch.empty((w.B, w.H, w.Tq, w.dv), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((w.B, w.H, w.Tq), dtype=torch.float32, device=dev)
-    dq, dk, dvg = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-
-    flush = torch.empty(args.flush_mib << 18, dtype=torch.float32, device=dev) if args.flush_mib > 0 else None
-
-    def step():
-        if flush is not None:
-            flush.fill_(1.0)
-        attn.fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse)
-        attn.bwd(q, k, v, o, lse, do, scale=w.scale, causal=w.causal, dq=dq, dk=dk, dv=dvg)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
-
-    attn.profile_start()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    attn.profile_stop()
-    kern = {name: attn.profile_query(kind) for kind, name in attn.KERNEL_NAMES.items()}
-
+    kern, ms_step = time_steps(attn, w, dev, args.steps, args.warmup, args.flush_mib)
     pairs, fwd_fl, bwd_fl, fwd_b, bwd_b = work(w)
-    ms_step = (t1 - t0) * 1e3 / args.steps
     fwd_ms = (kern["fwd"][0] + kern["fwd_aux"][0]) / args.steps
     bwd_ms = (kern["bwd_prep"][0] + kern["bwd_dkdv"][0] + kern["bwd_dq"][0]) / args.steps
-    if flush is not None:
-        ms_step = fwd_ms + bwd_ms  # the flush between steps is not attention work
     total_tflops = (fwd_fl + bwd_fl) / (ms_step * 1e-3) / 1e12
     fwd_tflops = fwd_fl / (fwd_ms * 1e-3) / 1e12 if fwd_ms > 0 else None
     bwd_tflops = bwd_fl / (bwd_ms * 1e-3) / 1e12 if bwd_ms > 0 else None
 
     # dominant kernel: largest recorded time
     kfl = kernel_flops(w)
+    kby = kernel_bytes(w)
     dom = max(("fwd", "bwd_dkdv", "bwd_dq"), key=lambda n: kern[n][0])
     dom_avg_ms = kern[dom][0] / max(1, kern[dom][1])
     alg_fl, exe_fl = kfl[dom]
@@ -442,13 +502,26 @@ def main(argv=None) -> int:
         "algorithmic_flops_per_launch": alg_fl,
         "executed_flops_per_launch": exe_fl,
         "executed_tflops": round(exe_fl / (dom_avg_ms * 1e-3) / 1e12, 2),
-        "algorithmic_bytes_per_launch": fwd_b if dom == "fwd" else bwd_b,
+        "algorithmic_bytes_per_launch": kby[dom],
+        "traffic_over_algorithmic_bytes": round(traffic / kby[dom], 3) if traffic else None,
     }
 
-    cpu = None
-    if args.cpu_budget > 0:
-        print(f"[bench] timing the CPU oracle (~{args.cpu_budget:.0f} s)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w, args.cpu_budget)
+    # the backward target workload, timed in the same run with the same step counts
+    targets = {w.name: {"fwd_frac_of_peak": round(fwd_tflops / PEAK_BF16_TFLOPS, 4) if fwd_tflops else None,
+                        "bwd_frac_of_peak": round(bwd_tflops / PEAK_BF16_TFLOPS, 4) if bwd_tflops else None}}
+    if args.targets and w.name == HEADLINE:
+        wt = WORKLOADS[BWD_TARGET]
+        kt, _ = time_steps(attn, wt, dev, args.steps, args.warmup, args.flush_mib)
+        _, tf_fl, tb_fl, _, _ = work(wt)
+        t_fwd_ms = (kt["fwd"][0] + kt["fwd_aux"][0]) / args.steps
+        t_bwd_ms = (kt["bwd_prep"][0] + kt["bwd_dkdv"][0] + kt["bwd_dq"][0]) / args.steps
+        targets[wt.name] = {
+            "fwd_ms": round(t_fwd_ms, 4),
+            "fwd_frac_of_peak": round(tf_fl / (t_fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "bwd_ms": round(t_bwd_ms, 4),
+            "bwd_frac_of_peak": round(tb_fl / (t_bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "kernel_ms_per_step": {n: round(kt[n][0] / args.steps, 4) for n in kt if kt[n][1]},
+        }
 
     line = {
         "metric": METRIC,
@@ -465,13 +538,14 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Tq": w.Tq, "Tk": w.Tk, "d": w.d, "dv": w.dv,
                    "causal": w.causal, "step": "attn_fwd + attn_bwd",
-                   **({"flush_mib_between_steps": args.flush_mib} if flush is not None else {})},
+                   **({"flush_mib_between_steps": args.flush_mib} if args.flush_mib > 0 else {})},
         "fwd_tflops": round(fwd_tflops, 2) if fwd_tflops else None,
         "fwd_frac_of_peak": round(fwd_tflops / PEAK_BF16_TFLOPS, 4) if fwd_tflops else None,
         "bwd_tflops": round(bwd_tflops, 2) if bwd_tflops else None,
         "bwd_frac_of_peak": round(bwd_tflops / PEAK_BF16_TFLOPS, 4) if bwd_tflops else None,
         "fwd_bwd_frac_of_peak": round(total_tflops / PEAK_BF16_TFLOPS, 4),
         "kernel_ms_per_step": {n: round(kern[n][0] / args.steps, 4) for n in kern},
+        "targets": targets,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -113,7 +113,23 @@ def _dims(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
     return B, H, Tq, k.shape[2], d, v.shape[3]
 
 
-def _need(t: torch.Tensor, name: str, dtype: torch.dtype, device) -> None:
+def _shapes(**named) -> None:
+    """Refuse caller-supplied buffers whose shape differs from the one the
+    call's dimensions imply (name=(tensor or None, shape)); runs before any
+    other check, so a mismatch is reported as such."""
+    for name, (t, shape) in named.items():
+        if t is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, device, shape=None) -> None:
+    """Check a tensor handed to the library: dtype, device, contiguity and,
+    when given, its exact shape (the kernels read and write the full extent
+    the dimensions imply, so a smaller buffer would be overrun)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if t.device.type != "cuda" or t.device != device:
@@ -126,6 +142,7 @@ def fwd(q, k, v, scale=None, causal=False, out=None, lse=None, num_splits=None):
     """bf16 forward: returns (o [B,H,Tq,dv] bf16, lse [B,H,Tq] fp32)."""
     lib = load()
     B, H, Tq, Tk, d, dv = _dims(q, k, v)
+    _shapes(out=(out, (B, H, Tq, dv)), lse=(lse, (B, H, Tq)))
     dev = q.device
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n, torch.bfloat16, dev)
@@ -135,8 +152,8 @@ def fwd(q, k, v, scale=None, causal=False, out=None, lse=None, num_splits=None):
         out = torch.empty((B, H, Tq, dv), dtype=torch.bfloat16, device=dev)
     if lse is None:
         lse = torch.empty((B, H, Tq), dtype=torch.float32, device=dev)
-    _need(out, "out", torch.bfloat16, dev)
-    _need(lse, "lse", torch.float32, dev)
+    _need(out, "out", torch.bfloat16, dev, (B, H, Tq, dv))
+    _need(lse, "lse", torch.float32, dev, (B, H, Tq))
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Tq, Tk, d, dv, float(scale), int(bool(causal)))
     if num_splits is None:
         _check("attn_fwd", lib.attn_fwd(*args, _stream(dev)))
@@ -150,23 +167,27 @@ def bwd(q, k, v, o, lse, dout, scale=None, causal=False, dq=None, dk=None, dv=No
     dlse (optional, fp32 [B,H,Tq]): upstream gradient on the LSE output."""
     lib = load()
     B, H, Tq, Tk, d, dvd = _dims(q, k, v)
+    _shapes(o=(o, (B, H, Tq, dvd)), dout=(dout, (B, H, Tq, dvd)), lse=(lse, (B, H, Tq)), dq=(dq, (B, H, Tq, d)),
+            dk=(dk, (B, H, Tk, d)), dv=(dv, (B, H, Tk, dvd)), dlse=(dlse, (B, H, Tq)))
     dev = q.device
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n, torch.bfloat16, dev)
-    _need(lse, "lse", torch.float32, dev)
+    _need(o, "o", torch.bfloat16, dev, (B, H, Tq, dvd))
+    _need(dout, "dout", torch.bfloat16, dev, (B, H, Tq, dvd))
+    _need(lse, "lse", torch.float32, dev, (B, H, Tq))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
-        _need(t, n, torch.bfloat16, dev)
+    for t, n, shp in ((dq, "dq", (B, H, Tq, d)), (dk, "dk", (B, H, Tk, d)), (dv, "dv", (B, H, Tk, dvd))):
+        _need(t, n, torch.bfloat16, dev, shp)
     tail = (_ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), B, H, Tq, Tk, d, dvd, float(scale), int(bool(causal)),
             _stream(dev))
     if dlse is None:
         _check("attn_bwd", lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), *tail))
     else:
-        _need(dlse, "dlse", torch.float32, dev)
+        _need(dlse, "dlse", torch.float32, dev, (B, H, Tq))
         _check("attn_bwd_dlse", lib.attn_bwd_dlse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dlse), *tail))
     return dq, dk, dv
 
@@ -212,6 +233,7 @@ def fwd_standard(q, k, v, scale=None, causal=False, out=None, lse=None):
     and out, as fwd): returns (o, lse).  For the IO comparison."""
     lib = load()
     B, H, Tq, Tk, d, dv = _dims(q, k, v)
+    _shapes(out=(out, (B, H, Tq, dv)), lse=(lse, (B, H, Tq)))
     dev = q.device
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n, torch.bfloat16, dev)
@@ -219,8 +241,8 @@ def fwd_standard(q, k, v, scale=None, causal=False, out=None, lse=None):
         scale = 1.0 / math.sqrt(d)
     out = torch.empty((B, H, Tq, dv), dtype=torch.bfloat16, device=dev) if out is None else out
     lse = torch.empty((B, H, Tq), dtype=torch.float32, device=dev) if lse is None else lse
-    _need(out, "out", torch.bfloat16, dev)
-    _need(lse, "lse", torch.float32, dev)
+    _need(out, "out", torch.bfloat16, dev, (B, H, Tq, dv))
+    _need(lse, "lse", torch.float32, dev, (B, H, Tq))
     rc = lib.attn_fwd_standard(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Tq, Tk, d, dv, float(scale),
                                int(bool(causal)), _stream(dev))
     _check("attn_fwd_standard", rc)
@@ -234,21 +256,20 @@ def decode(q, k, v, kv_lens=None, scale=None, causal=False, out=None, lse=None, 
     (o [B,H,Tq,dv] bf16, lse [B,H,Tq] fp32)."""
     lib = load()
     B, H, Tq, Tk, d, dv = _dims(q, k, v)
+    _shapes(out=(out, (B, H, Tq, dv)), lse=(lse, (B, H, Tq)), kv_lens=(kv_lens, (B,)))
     dev = q.device
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n, torch.bfloat16, dev)
     if kv_lens is not None:
-        _need(kv_lens, "kv_lens", torch.int32, dev)
-        if kv_lens.shape != (B,):
-            raise ValueError(f"kv_lens must have shape ({B},), got {tuple(kv_lens.shape)}")
+        _need(kv_lens, "kv_lens", torch.int32, dev, (B,))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty((B, H, Tq, dv), dtype=torch.bfloat16, device=dev)
     if lse is None:
         lse = torch.empty((B, H, Tq), dtype=torch.float32, device=dev)
-    _need(out, "out", torch.bfloat16, dev)
-    _need(lse, "lse", torch.float32, dev)
+    _need(out, "out", torch.bfloat16, dev, (B, H, Tq, dv))
+    _need(lse, "lse", torch.float32, dev, (B, H, Tq))
     lens = 0 if kv_lens is None else _ptr(kv_lens)
     args = (_ptr(q), _ptr(k), _ptr(v), lens, _ptr(out), _ptr(lse), B, H, Tq, Tk, d, dv, float(scale),
             int(bool(causal)))
@@ -265,6 +286,7 @@ def fwd_f32(q, k, v, scale=None, causal=False, block_n=0, out=None, lse=None, re
     a running max: a negative control that overflows for large scores)."""
     lib = load()
     B, H, Tq, Tk, d, dv = _dims(q, k, v)
+    _shapes(out=(out, (B, H, Tq, dv)), lse=(lse, (B, H, Tq)))
     dev = q.device
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n, torch.float32, dev)
@@ -272,6 +294,8 @@ def fwd_f32(q, k, v, scale=None, causal=False, block_n=0, out=None, lse=None, re
         scale = 1.0 / math.sqrt(d)
     out = torch.empty((B, H, Tq, dv), dtype=torch.float32, device=dev) if out is None else out
     lse = torch.empty((B, H, Tq), dtype=torch.float32, device=dev) if lse is None else lse
+    _need(out, "out", torch.float32, dev, (B, H, Tq, dv))
+    _need(lse, "lse", torch.float32, dev, (B, H, Tq))
     fn = "attn_fwd_f32" if rescale else "attn_fwd_f32_unrescaled"
     rc = getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Tq, Tk, d, dv, float(scale),
                           int(bool(causal)), int(block_n), _stream(dev))
@@ -283,9 +307,13 @@ def bwd_f32(q, k, v, o, lse, dout, scale=None, causal=False):
     """fp32 backward: returns (dq, dk, dv)."""
     lib = load()
     B, H, Tq, Tk, d, dvd = _dims(q, k, v)
+    _shapes(o=(o, (B, H, Tq, dvd)), dout=(dout, (B, H, Tq, dvd)), lse=(lse, (B, H, Tq)))
     dev = q.device
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (dout, "dout")):
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n, torch.float32, dev)
+    _need(o, "o", torch.float32, dev, (B, H, Tq, dvd))
+    _need(dout, "dout", torch.float32, dev, (B, H, Tq, dvd))
+    _need(lse, "lse", torch.float32, dev, (B, H, Tq))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)

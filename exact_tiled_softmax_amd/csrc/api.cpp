@@ -77,10 +77,12 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
   if (!bf16_dims_supported(d, dv)) return ATTN_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int BH = B * H;
+  const int splits = attn::bwd_bf16_dq_splits(BH, Tq, Tk, d, SIZE_MAX);
   void* ws = nullptr;
-  hipError_t e = hipMallocAsync(&ws, attn::bwd_bf16_workspace_bytes(BH, Tq, Tk, d), s);
+  hipError_t e = hipMallocAsync(&ws, attn::bwd_bf16_workspace_bytes(BH, Tq, Tk, d, splits), s);
   if (e != hipSuccess) return hip_fail(e);
-  e = attn::bwd_bf16_launch(q, k, v, o, lse, dlse, dout, dq, dk, dv_grad, BH, Tq, Tk, d, scale, causal, ws, s);
+  e = attn::bwd_bf16_launch(q, k, v, o, lse, dlse, dout, dq, dk, dv_grad, BH, Tq, Tk, d, scale, causal, splits, ws,
+                            s);
   hipError_t f = hipFreeAsync(ws, s);
   if (e == hipSuccess) e = f;
   return e == hipSuccess ? ATTN_OK : hip_fail(e);

@@ -46,11 +46,15 @@ hipError_t merge_states_launch(const float* acc, const float* m, const float* l,
                                int Tq, int d, hipStream_t stream);
 
 // ---- bf16 backward --------------------------------------------------------------
-size_t bwd_bf16_workspace_bytes(int BH, int Tq, int Tk, int d);
+// Key-range splits of the dQ kernel for a workspace of at most ws_cap bytes:
+// the default plan when it fits, else the most splits that fit (1 = no fp32
+// partials), 0 if not even the row statistics fit.
+int bwd_bf16_dq_splits(int BH, int Tq, int Tk, int d, size_t ws_cap);
+size_t bwd_bf16_workspace_bytes(int BH, int Tq, int Tk, int d, int dq_splits);
 // dlse (may be null): upstream gradient of the loss with respect to LSE [BH][Tq].
 hipError_t bwd_bf16_launch(const void* q, const void* k, const void* v, const void* o, const float* lse,
                            const float* dlse, const void* dout, void* dq, void* dk, void* dv, int BH, int Tq, int Tk,
-                           int d, float scale, int causal, void* workspace, hipStream_t stream);
+                           int d, float scale, int causal, int dq_splits, void* workspace, hipStream_t stream);
 
 // ---- bf16 decode (newest 1..4 queries against a key cache) -----------------------
 int decode_bf16_num_splits(int BH, int Tk, int d, int requested);

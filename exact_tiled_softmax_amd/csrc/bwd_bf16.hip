@@ -63,37 +63,44 @@ struct BwdArgs {
 };
 
 // ---------------------------------------------------------------------------------
-// bwd_stats: 16 lanes per query row (padded to a multiple of 32 rows per head).
+// bwd_stats: 16 lanes per query row (padded to a multiple of 32 rows per head),
+// rows walked with a 64-bit grid stride so that any B*H*Tq the ABI accepts is
+// covered.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_stats_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ dout,
                                                         const float* __restrict__ lse, const float* __restrict__ dlse,
                                                         float* __restrict__ stats, int BH, int Tq, int nqb32) {
   constexpr int PER = D / 16;
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  const int row = t / 16, sub = t % 16;
-  const int rows_pad = nqb32 * 32;
-  const int bh = row / rows_pad, qi = row % rows_pad;
-  const bool in_grid = bh < BH;
-  const bool ok = in_grid && qi < Tq;
-  float acc = 0.f;
-  if (ok) {
-    const size_t base = ((size_t)bh * Tq + qi) * D + sub * PER;
-    const uint16_t* op = reinterpret_cast<const uint16_t*>(o) + base;
-    const uint16_t* dp = reinterpret_cast<const uint16_t*>(dout) + base;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) acc += bf16_to_f32(op[j]) * bf16_to_f32(dp[j]);
-  }
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
-  if (in_grid && sub == 0) {
-    float l2 = INFINITY;
+  const int sub = threadIdx.x % 16;
+  const size_t rows_pad = (size_t)nqb32 * 32;
+  const size_t n_rows = (size_t)BH * rows_pad;
+  const size_t stride = (size_t)gridDim.x * (blockDim.x / 16);
+  // the trip count is uniform across the 16 lanes of a row (a whole row per
+  // 16-lane group), so the shuffles below see all of their lanes
+  for (size_t row = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) / 16; row < n_rows; row += stride) {
+    const size_t bh = row / rows_pad;
+    const int qi = (int)(row % rows_pad);
+    const bool ok = qi < Tq;
+    float acc = 0.f;
     if (ok) {
-      const float l = lse[(size_t)bh * Tq + qi];
-      l2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
+      const size_t base = (bh * Tq + qi) * D + sub * PER;
+      const uint16_t* op = reinterpret_cast<const uint16_t*>(o) + base;
+      const uint16_t* dp = reinterpret_cast<const uint16_t*>(dout) + base;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) acc += bf16_to_f32(op[j]) * bf16_to_f32(dp[j]);
     }
-    float* blk = stats + ((size_t)bh * nqb32 + qi / 32) * 64;
-    blk[qi % 32] = l2;
-    blk[32 + qi % 32] = ok ? acc - (dlse ? dlse[(size_t)bh * Tq + qi] : 0.f) : 0.f;
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
+    if (sub == 0) {
+      float l2 = INFINITY;
+      if (ok) {
+        const float l = lse[bh * Tq + qi];
+        l2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
+      }
+      float* blk = stats + (bh * nqb32 + qi / 32) * 64;
+      blk[qi % 32] = l2;
+      blk[32 + qi % 32] = ok ? acc - (dlse ? dlse[bh * Tq + qi] : 0.f) : 0.f;
+    }
   }
 }
 
@@ -623,7 +630,7 @@ struct DqSplit {
   int splits, tiles_per_split;
 };
 
-DqSplit dq_split(int BH, int Tq, int Tk) {
+int dq_default_splits(int BH, int Tq, int Tk) {
   const int nqb = (Tq + 255) / 256;
   const int nkt = (Tk + 63) / 64;
   const long long items = (long long)BH * nqb;
@@ -632,6 +639,13 @@ DqSplit dq_split(int BH, int Tq, int Tk) {
     s = (int)((1024 + items - 1) / items);
     s = std::min(s, std::max(1, nkt / 8));
   }
+  return s;
+}
+
+// s requested splits -> tiles per split, and the splits that are non-empty
+DqSplit dq_split(int Tk, int s) {
+  const int nkt = (Tk + 63) / 64;
+  s = std::max(1, std::min(s, nkt));
   const int tps = (nkt + s - 1) / s;
   return {(nkt + tps - 1) / tps, tps};
 }
@@ -640,11 +654,10 @@ struct BwdLayout {
   size_t stats, dq_part, total;
 };
 
-BwdLayout bwd_layout(int BH, int Tq, int Tk, int d) {
+BwdLayout bwd_layout(int BH, int Tq, int Tk, int d, int dq_splits) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   const size_t nqb32 = (size_t)(Tq + 31) / 32;
-  const size_t tk_pad = (size_t)(Tk + 63) / 64 * 64;
-  const DqSplit sp = dq_split(BH, Tq, Tk);
+  const DqSplit sp = dq_split(Tk, dq_splits);
   BwdLayout L;
   L.stats = 0;
   L.dq_part = up(L.stats + (size_t)BH * nqb32 * 64 * sizeof(float));
@@ -658,9 +671,11 @@ hipError_t bwd_launch_d(BwdArgs& args, const __bf16* o, const float* lse, const 
   // pre-pass: row statistics
   prof_begin(2, stream);
   {
-    const int rows = args.BH * args.nqb32 * 32;
-    hipLaunchKernelGGL(bwd_stats_kernel<D>, dim3((rows * 16 + 255) / 256), dim3(256), 0, stream, o, args.dout, lse,
-                       dlse, reinterpret_cast<float*>(ws + L.stats), args.BH, args.Tq, args.nqb32);
+    // 16 rows per 256-thread block; at most 2^20 blocks, striding beyond
+    const size_t rows = (size_t)args.BH * args.nqb32 * 32;
+    const unsigned blocks = (unsigned)std::min<size_t>((rows + 15) / 16, (size_t)1 << 20);
+    hipLaunchKernelGGL(bwd_stats_kernel<D>, dim3(blocks), dim3(256), 0, stream, o, args.dout, lse, dlse,
+                       reinterpret_cast<float*>(ws + L.stats), args.BH, args.Tq, args.nqb32);
   }
   prof_end(2, stream);
   hipError_t e = hipGetLastError();
@@ -700,12 +715,27 @@ hipError_t bwd_launch_d(BwdArgs& args, const __bf16* o, const float* lse, const 
 
 }  // namespace
 
-size_t bwd_bf16_workspace_bytes(int BH, int Tq, int Tk, int d) { return bwd_layout(BH, Tq, Tk, d).total; }
+int bwd_bf16_dq_splits(int BH, int Tq, int Tk, int d, size_t ws_cap) {
+  // the default plan, or the most splits whose partials still fit ws_cap
+  // (1: no partials); 0 when not even the row statistics fit.  Workspace
+  // grows with the split count, so the first fit going down is the largest.
+  int s = dq_default_splits(BH, Tq, Tk);
+  for (;;) {
+    const int eff = dq_split(Tk, s).splits;
+    if (bwd_layout(BH, Tq, Tk, d, eff).total <= ws_cap) return eff;
+    if (eff <= 1) return 0;
+    s = eff - 1;
+  }
+}
+
+size_t bwd_bf16_workspace_bytes(int BH, int Tq, int Tk, int d, int dq_splits) {
+  return bwd_layout(BH, Tq, Tk, d, dq_splits).total;
+}
 
 hipError_t bwd_bf16_launch(const void* q, const void* k, const void* v, const void* o, const float* lse,
                            const float* dlse, const void* dout, void* dq, void* dk, void* dv, int BH, int Tq, int Tk,
-                           int d, float scale, int causal, void* workspace, hipStream_t stream) {
-  const BwdLayout L = bwd_layout(BH, Tq, Tk, d);
+                           int d, float scale, int causal, int dq_splits, void* workspace, hipStream_t stream) {
+  const BwdLayout L = bwd_layout(BH, Tq, Tk, d, dq_splits);
   char* ws = static_cast<char*>(workspace);
   BwdArgs a;
   a.q = static_cast<const __bf16*>(q);
@@ -720,7 +750,7 @@ hipError_t bwd_bf16_launch(const void* q, const void* k, const void* v, const vo
   a.Tq = Tq;
   a.Tk = Tk;
   a.nqb32 = (Tq + 31) / 32;
-  const DqSplit sp = dq_split(BH, Tq, Tk);
+  const DqSplit sp = dq_split(Tk, dq_splits);
   a.dq_splits = sp.splits;
   a.dq_head_group = head_group(BH, ((Tq + DqCfg<128>::BM - 1) / DqCfg<128>::BM) * sp.splits);
   a.dq_tiles_per_split = sp.tiles_per_split;

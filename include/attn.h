@@ -39,6 +39,18 @@
  *           score of -infinity.
  * Scale.    `scale` multiplies Q K^T; callers normally pass 1/sqrt(d).  It
  *           must be finite and >= 0.
+ * Values.   Every element of q, k, v and dout (and o, lse, dlse passed to a
+ *           backward, as a forward returned them) must be finite.  A score of
+ *           -infinity arises only from the mask, where a blocked key counts
+ *           as a score of -infinity ("Tiled attention with an online
+ *           softmax", section "Task").  NaN or infinite inputs are outside the
+ *           domain: the bf16 forward kernels are compiled without NaN
+ *           semantics (a row maximum may then ignore a NaN score), so such
+ *           inputs give unspecified outputs, never an error code.  Nothing
+ *           reads the inputs on the host to check this.
+ * Sizes.    B, H, Tq, Tk, d, dv >= 1, with B*H <= 2^31/8 - 1 and B*H*Tq and
+ *           B*H*Tk each <= 2^31 - 1 (row counts, not element counts: element
+ *           offsets are 64-bit inside); otherwise ATTN_ERR_INVALID_ARG.
  * Empty rows. A query row with no allowed key gets O = 0 and LSE = -inf
  *           (the page's step leaves such a row at m = -inf, l = 0, a = 0).
  *           With causal top-left masking and Tk >= 1 this never happens.
@@ -77,7 +89,7 @@ extern "C" {
  * Arithmetic: bf16 MFMA products with fp32 accumulation; the online softmax
  * statistics are fp32; P is rounded to bf16 before the P V product.
  * Supported: d == dv, d in {64, 128}; otherwise ATTN_ERR_UNSUPPORTED.
- * B, H, Tq, Tk >= 1 (any value; ragged tails are masked).
+ * B, H, Tq, Tk >= 1 within the size limits above; ragged tails are masked.
  * Workspace: none, except the partial states when the key range is split
  * (num_splits*B*H*Tq*(dv+2) floats).
  */

@@ -179,3 +179,73 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(attn, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         attn.load()
+
+
+# ---- the binding refuses wrongly shaped buffers before any launch ----------
+# (CPU tensors: the shape check runs first, so these need no GPU)
+
+def _bf(*shape):
+    import torch
+    return torch.zeros(shape, dtype=torch.bfloat16)
+
+
+def _f32(*shape):
+    import torch
+    return torch.zeros(shape, dtype=torch.float32)
+
+
+B_, H_, TQ_, TK_, D_ = 2, 3, 40, 50, 64
+
+
+@pytest.mark.parametrize("which,bad", [("out", (B_, H_, TQ_ - 1, D_)), ("out", (B_, H_, TQ_, D_ * 2)),
+                                       ("lse", (B_, H_, TQ_ - 1)), ("lse", (B_, H_, TQ_, 1))])
+def test_fwd_refuses_misshaped_outputs(lib, which, bad):
+    q, k, v = _bf(B_, H_, TQ_, D_), _bf(B_, H_, TK_, D_), _bf(B_, H_, TK_, D_)
+    kw = {which: (_bf(*bad) if which == "out" else _f32(*bad))}
+    with pytest.raises(ValueError, match=f"{which} must have shape"):
+        attn.fwd(q, k, v, **kw)
+    with pytest.raises(ValueError, match=f"{which} must have shape"):
+        attn.fwd_standard(q, k, v, **kw)
+
+
+@pytest.mark.parametrize("which", ["o", "dout", "lse", "dq", "dk", "dv", "dlse"])
+def test_bwd_refuses_misshaped_buffers(lib, which):
+    q, k, v = _bf(B_, H_, TQ_, D_), _bf(B_, H_, TK_, D_), _bf(B_, H_, TK_, D_)
+    args = dict(o=_bf(B_, H_, TQ_, D_), lse=_f32(B_, H_, TQ_), dout=_bf(B_, H_, TQ_, D_))
+    # dk and dv have the key count, dq the query count: swapping them must fail
+    bad = {"o": _bf(B_, H_, TK_, D_), "dout": _bf(B_, H_, TQ_, D_ + 8), "lse": _f32(B_, H_, TK_),
+           "dq": _bf(B_, H_, TK_, D_), "dk": _bf(B_, H_, TQ_, D_), "dv": _bf(B_, H_, TK_ - 1, D_),
+           "dlse": _f32(B_, H_ + 1, TQ_)}[which]
+    kw = {}
+    if which in args:
+        args[which] = bad
+    else:
+        kw[which] = bad
+    with pytest.raises(ValueError, match=f"{which} must have shape"):
+        attn.bwd(q, k, v, args["o"], args["lse"], args["dout"], **kw)
+
+
+def test_f32_and_decode_refuse_misshaped_buffers(lib):
+    import torch
+    q, k, v = _f32(1, 2, 9, 16), _f32(1, 2, 11, 16), _f32(1, 2, 11, 16)
+    with pytest.raises(ValueError, match="lse must have shape"):
+        attn.fwd_f32(q, k, v, lse=_f32(1, 2, 8))
+    with pytest.raises(ValueError, match="o must have shape"):
+        attn.bwd_f32(q, k, v, _f32(1, 2, 11, 16), _f32(1, 2, 9), _f32(1, 2, 9, 16))
+    qd, kd, vd = _bf(3, 2, 1, 64), _bf(3, 2, 100, 64), _bf(3, 2, 100, 64)
+    with pytest.raises(ValueError, match="kv_lens must have shape"):
+        attn.decode(qd, kd, vd, kv_lens=torch.zeros(2, dtype=torch.int32))
+    with pytest.raises(ValueError, match="out must have shape"):
+        attn.decode(qd, kd, vd, out=_bf(3, 2, 2, 64))
+
+
+def test_backward_row_count_limit_is_the_abi_limit(lib):
+    # the largest B*H*Tq the ABI accepts: argument checks pass (the call then
+    # stops at the first null pointer check, before any HIP call), and one
+    # row more is refused
+    nz = NZ
+    rows_max = 2**31 - 1
+    assert lib.attn_bwd(nz, nz, nz, nz, nz, nz, nz, nz, None, 1, 1, rows_max, 8, 64, 64, 0.125, 0, None) \
+        == attn.ATTN_ERR_INVALID_ARG  # null dv_grad
+    assert lib.attn_bwd(nz, nz, nz, nz, nz, nz, nz, nz, nz, 2, 1, rows_max, 8, 64, 64, 0.125, 0, None) \
+        == attn.ATTN_ERR_INVALID_ARG  # B*H*Tq past 2^31 - 1
