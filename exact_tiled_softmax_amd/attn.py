@@ -20,8 +20,10 @@ ATTN_OK = 0
 ATTN_ERR_INVALID_ARG = -1
 ATTN_ERR_UNSUPPORTED = -2
 ATTN_ERR_HIP = -3
+ATTN_ERR_TOO_LARGE = -4
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
-EXPORTED = ("attn_fwd", "attn_fwd_splits", "attn_bwd", "attn_bwd_dlse", "attn_fwd_state", "attn_merge_states",
+EXPORTED = ("attn_fwd", "attn_fwd_splits", "attn_bwd", "attn_bwd_noalloc", "attn_bwd_dlse", "attn_fwd_state", "attn_merge_states",
             "attn_decode", "attn_decode_splits", "attn_fwd_standard", "attn_fwd_f32", "attn_fwd_f32_unrescaled", "attn_bwd_f32", "attn_strerror", "attn_last_hip_error", "attn_profile_start",
             "attn_profile_stop", "attn_profile_query")
 
@@ -58,6 +60,7 @@ def load() -> ctypes.CDLL:
     lib.attn_fwd.argtypes = [P, P, P, P, P, *dims, P]
     lib.attn_fwd_splits.argtypes = [P, P, P, P, P, *dims, I, P]
     lib.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, *dims, P]
+    lib.attn_bwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, *dims, P]
     lib.attn_bwd_dlse.argtypes = [P, P, P, P, P, P, P, P, P, P, *dims, P]
     lib.attn_fwd_state.argtypes = [P, P, P, P, P, P, *dims, I, I, P]
     lib.attn_merge_states.argtypes = [P, P, P, I, P, P, I, I, I, I, P]
@@ -67,7 +70,7 @@ def load() -> ctypes.CDLL:
     lib.attn_fwd_f32.argtypes = [P, P, P, P, P, *dims, I, P]
     lib.attn_fwd_f32_unrescaled.argtypes = [P, P, P, P, P, *dims, I, P]
     lib.attn_bwd_f32.argtypes = [P, P, P, P, P, P, P, P, P, *dims, P]
-    for fn in ("attn_fwd", "attn_fwd_splits", "attn_bwd", "attn_bwd_dlse", "attn_fwd_state", "attn_merge_states",
+    for fn in ("attn_fwd", "attn_fwd_splits", "attn_bwd", "attn_bwd_noalloc", "attn_bwd_dlse", "attn_fwd_state", "attn_merge_states",
                "attn_decode", "attn_decode_splits", "attn_fwd_standard", "attn_fwd_f32", "attn_fwd_f32_unrescaled", "attn_bwd_f32"):
         getattr(lib, fn).restype = I
     lib.attn_strerror.argtypes = [I]
@@ -162,9 +165,11 @@ def fwd(q, k, v, scale=None, causal=False, out=None, lse=None, num_splits=None):
     return out, lse
 
 
-def bwd(q, k, v, o, lse, dout, scale=None, causal=False, dq=None, dk=None, dv=None, dlse=None):
+def bwd(q, k, v, o, lse, dout, scale=None, causal=False, dq=None, dk=None, dv=None, dlse=None, noalloc=False):
     """bf16 backward: returns (dq, dk, dv) bf16 with the shapes of q, k, v.
-    dlse (optional, fp32 [B,H,Tq]): upstream gradient on the LSE output."""
+    dlse (optional, fp32 [B,H,Tq]): upstream gradient on the LSE output.
+    noalloc=True calls attn_bwd_noalloc (workspace in the library's static
+    scratch; no dlse)."""
     lib = load()
     B, H, Tq, Tk, d, dvd = _dims(q, k, v)
     _shapes(o=(o, (B, H, Tq, dvd)), dout=(dout, (B, H, Tq, dvd)), lse=(lse, (B, H, Tq)), dq=(dq, (B, H, Tq, d)),
@@ -184,7 +189,11 @@ def bwd(q, k, v, o, lse, dout, scale=None, causal=False, dq=None, dk=None, dv=No
         _need(t, n, torch.bfloat16, dev, shp)
     tail = (_ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), B, H, Tq, Tk, d, dvd, float(scale), int(bool(causal)),
             _stream(dev))
-    if dlse is None:
+    if noalloc:
+        if dlse is not None:
+            raise ValueError("attn_bwd_noalloc takes no dlse")
+        _check("attn_bwd_noalloc", lib.attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), *tail))
+    elif dlse is None:
         _check("attn_bwd", lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), *tail))
     else:
         _need(dlse, "dlse", torch.float32, dev, (B, H, Tq))

@@ -88,6 +88,26 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
 }
 
+// The backward with its workspace in the library's static scratch array: no
+// allocation of any kind.  Sizes are checked before any HIP call.
+int bwd_noalloc_impl(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                     void* dq, void* dk, void* dv_grad, int B, int H, int Tq, int Tk, int d, int dv, float scale,
+                     int causal, void* stream) {
+  int rc = check_common(q, k, v, o, lse, B, H, Tq, Tk, d, dv, scale);
+  if (rc != ATTN_OK) return rc;
+  if (!dout || !dq || !dk || !dv_grad) return ATTN_ERR_INVALID_ARG;
+  if (!bf16_dims_supported(d, dv)) return ATTN_ERR_UNSUPPORTED;
+  const int BH = B * H;
+  const int splits = attn::bwd_bf16_dq_splits(BH, Tq, Tk, d, ATTN_NOALLOC_SCRATCH_BYTES);
+  if (splits < 1) return ATTN_ERR_TOO_LARGE;
+  void* scratch = nullptr;
+  hipError_t e = attn::bwd_bf16_noalloc_scratch(&scratch);
+  if (e != hipSuccess) return hip_fail(e);
+  e = attn::bwd_bf16_launch(q, k, v, o, lse, nullptr, dout, dq, dk, dv_grad, BH, Tq, Tk, d, scale, causal, splits,
+                            scratch, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : hip_fail(e);
+}
+
 int decode_impl(const void* q, const void* k, const void* v, const int* kv_lens, void* o, float* lse, int B, int H,
                 int Tq, int Tk, int d, int dv, float scale, int causal, int num_splits, void* stream) {
   int rc = check_common(q, k, v, o, lse, B, H, Tq, Tk, d, dv, scale);
@@ -231,6 +251,12 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   return bwd_impl(q, k, v, o, lse, nullptr, dout, dq, dk, dv_grad, B, H, Tq, Tk, d, dv, scale, causal, stream);
 }
 
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                     void* dq, void* dk, void* dv_grad, int B, int H, int Tq, int Tk, int d, int dv, float scale,
+                     int causal, void* stream) {
+  return bwd_noalloc_impl(q, k, v, o, lse, dout, dq, dk, dv_grad, B, H, Tq, Tk, d, dv, scale, causal, stream);
+}
+
 int attn_bwd_dlse(const void* q, const void* k, const void* v, const void* o, const float* lse, const float* dlse,
                   const void* dout, void* dq, void* dk, void* dv_grad, int B, int H, int Tq, int Tk, int d, int dv,
                   float scale, int causal, void* stream) {
@@ -335,6 +361,9 @@ const char* attn_strerror(int code) {
       return "unsupported head dimensions for this entry point";
     case ATTN_ERR_HIP:
       return "a HIP launch or allocation failed (see attn_last_hip_error)";
+    case ATTN_ERR_TOO_LARGE:
+      return "the problem needs more scratch memory than the no-allocation entry point holds "
+             "(ATTN_NOALLOC_SCRATCH_BYTES)";
     default:
       return "unknown error code";
   }

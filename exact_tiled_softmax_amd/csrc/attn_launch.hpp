@@ -55,6 +55,9 @@ size_t bwd_bf16_workspace_bytes(int BH, int Tq, int Tk, int d, int dq_splits);
 hipError_t bwd_bf16_launch(const void* q, const void* k, const void* v, const void* o, const float* lse,
                            const float* dlse, const void* dout, void* dq, void* dk, void* dv, int BH, int Tq, int Tk,
                            int d, float scale, int causal, int dq_splits, void* workspace, hipStream_t stream);
+// Device address of this device's copy of the library's static scratch array
+// (ATTN_NOALLOC_SCRATCH_BYTES bytes), looked up once per device.
+hipError_t bwd_bf16_noalloc_scratch(void** ptr);
 
 // ---- bf16 decode (newest 1..4 queries against a key cache) -----------------------
 int decode_bf16_num_splits(int BH, int Tk, int d, int requested);

@@ -37,6 +37,9 @@
 // tiles are copied global -> LDS by the direct-to-LDS vector load, several
 // tiles ahead of the compute.
 #include <algorithm>
+#include <mutex>
+
+#include "attn.h"
 
 #include "attn_common.hpp"
 #include "attn_launch.hpp"
@@ -760,6 +763,35 @@ hipError_t bwd_bf16_launch(const void* q, const void* k, const void* v, const vo
   const __bf16* ob = static_cast<const __bf16*>(o);
   return d == 128 ? bwd_launch_d<128>(a, ob, lse, dlse, causal != 0, ws, L, stream)
                   : bwd_launch_d<64>(a, ob, lse, dlse, causal != 0, ws, L, stream);
+}
+
+// ---- scratch memory of the entry point that allocates nothing -------------------
+// A file-scope device array: every GPU the library runs on holds its own copy
+// until the process ends.  Host code never uses the array's name as an
+// address (on the host it is only a stand-in): the device address of each
+// GPU's copy comes from hipGetSymbolAddress, taken once per device on that
+// device's first call and kept.
+namespace {
+__device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+}  // namespace
+
+hipError_t bwd_bf16_noalloc_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> g(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace attn

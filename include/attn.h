@@ -78,6 +78,7 @@ extern "C" {
 #define ATTN_ERR_INVALID_ARG (-1) /* null pointer, dimension < 1, bad scale, bad block size */
 #define ATTN_ERR_UNSUPPORTED (-2) /* head dims the bf16 kernels are not built for */
 #define ATTN_ERR_HIP (-3)         /* a HIP launch or allocation failed */
+#define ATTN_ERR_TOO_LARGE (-4)   /* attn_bwd_noalloc: workspace larger than its static scratch */
 
 /*
  * attn_fwd - bf16 forward.
@@ -134,6 +135,32 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
              const void* dout, void* dq, void* dk, void* dv_grad,
              int B, int H, int Tq, int Tk, int d, int dv, float scale, int causal,
              void* stream);
+
+/*
+ * attn_bwd_noalloc - attn_bwd that allocates nothing: for callers that cannot
+ * allocate device memory during the call (code under HIP graph capture,
+ * tight training or serving loops, harnesses that forbid hipMalloc).
+ *   Arguments, layouts, results and supported sizes as attn_bwd.  Its
+ *   workspace (row statistics and, for few query blocks against many keys,
+ *   fp32 partial dQ of the key-range splits) lives in a static scratch array
+ *   of ATTN_NOALLOC_SCRATCH_BYTES bytes that the library holds on every GPU
+ *   it runs on until the process ends; nothing in it needs clearing (every
+ *   call overwrites what it reads).  The split count is attn_bwd's when its
+ *   partials fit, else the largest that fits (the summation order of dQ, and
+ *   so its last bits, can then differ from attn_bwd's).
+ *   ATTN_ERR_TOO_LARGE (checked before any HIP call) when not even the row
+ *   statistics fit: about B*H*Tq*8 bytes, i.e. B*H*Tq above about 8.4 million
+ *   rows.  The first call on a device looks up the device address of that
+ *   device's copy (hipGetSymbolAddress) and keeps it.
+ *   Calls on one GPU share its scratch: two calls whose work overlaps in time
+ *   on one GPU (different streams, or host threads) race and corrupt each
+ *   other's gradients; serialise them on one stream.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES (64u << 20)
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv_grad,
+                     int B, int H, int Tq, int Tk, int d, int dv, float scale, int causal,
+                     void* stream);
 
 /*
  * attn_bwd_dlse - attn_bwd with an upstream gradient on the LSE output.
