@@ -36,6 +36,8 @@
 // With key splits, each workgroup covers one contiguous key range and stores
 // its unnormalised state (m, l, a) in fp32; a second kernel merges the states
 // of a row with the same rescale rule and writes O and LSE.
+#include <type_traits>
+
 #include "attn_common.hpp"
 #include "attn_launch.hpp"
 #include "tile_stream.hpp"
@@ -109,15 +111,47 @@ __device__ __forceinline__ void fwd_issue(const FwdArgs& a, int bh, int key0, __
 // scaling the scores in place and writing -inf for blocked ones, after which
 // the shared code runs with a unit scale: exp2(-inf - mu) = 0 exactly, also
 // when scale == 0.  A row with no allowed key yet (m_ref = -inf) uses mu = 0.
+//
+// LDS addresses are a per-lane byte offset, computed once per kernel
+// (FwdLdsOffsets), plus a constant: the stage base is a compile-time constant
+// (the tile loop is unrolled over the stages) and the rows of a fragment
+// group differ from the first group's by whole 16-row blocks, which the
+// swizzle leaves unchanged.
 template <int D>
-__device__ __forceinline__ void fwd_tile(const __bf16* stg, const bf16x8 (&qf)[8], f32x16 (&acc)[4], float& m_ref,
-                                         float& l_run, float c, int lane, bool need_mask, int key0, int kend, int row,
-                                         bool causal) {
+struct FwdLdsOffsets {
+  uint32_t k[D / 16];          // K fragment of k-step ks, rows 0..31 (+32u rows for block u)
+  uint32_t v[D / 32][2];       // V^T fragment of column block cb, rows 4hf..+3 (h = 0) and 8 more (h = 1)
+};
+
+template <int D>
+__device__ __forceinline__ FwdLdsOffsets<D> fwd_lds_offsets(int lane) {
   using C = FwdCfg<D>;
-  const int lr = lane % 32, hf = lane / 32;
-  const __bf16* Ks = stg;
-  const __bf16* Vs = stg + C::TILE;
-  const int rsw = swz<C::CPR>(lr);
+  const int lr = lane % 32, hf = lane / 32, rsw = swz<C::CPR>(lr);
+  const int g16 = lane % 16, csub = (lane / 16) % 2;
+  auto at = [](int r, int cc) { return r * D + 8 * ((cc >> 3) ^ swz<C::CPR>(r)) + (cc & 7); };
+  FwdLdsOffsets<D> o;
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) o.k[ks] = (uint32_t)(lr * D + 8 * ((2 * ks + hf) ^ rsw)) * 2u;
+#pragma unroll
+  for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      o.v[cb][h] = (uint32_t)(C::TILE + at(4 * hf + g16 / 4 + 8 * h, 32 * cb + 16 * csub + 4 * (g16 % 4))) * 2u;
+  // opaque to the compiler's known-bits analysis, so that base + constant
+  // stays an add, which folds into the LDS instruction's offset field
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) asm volatile("" : "+v"(o.k[ks]));
+#pragma unroll
+  for (int cb = 0; cb < C::CB; ++cb) asm volatile("" : "+v"(o.v[cb][0]), "+v"(o.v[cb][1]));
+  return o;
+}
+
+template <int D>
+__device__ __forceinline__ void fwd_tile(const char* stg, const FwdLdsOffsets<D>& lo, const bf16x8 (&qf)[8],
+                                         f32x16 (&acc)[4], float& m_ref, float& l_run, float c, int lane,
+                                         bool need_mask, int key0, int kend, int row, bool causal) {
+  using C = FwdCfg<D>;
+  const int hf = lane / 32;
   // the two 32-key score chains alternate; K fragments are read 4 k-steps
   // ahead of their MFMAs (each read issued after the MFMA that frees its
   // registers)
@@ -125,7 +159,8 @@ __device__ __forceinline__ void fwd_tile(const __bf16* stg, const bf16x8 (&qf)[8
   bf16x8 kfr[C::KS][2];
   auto rd = [&](int ks) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) kfr[ks][u] = ld16(Ks + (32 * u + lr) * D + 8 * ((2 * ks + hf) ^ rsw));
+    for (int u = 0; u < 2; ++u)
+      kfr[ks][u] = *reinterpret_cast<const bf16x8*>(stg + lo.k[ks] + 32 * u * D * 2);
   };
 #pragma unroll
   for (int ks = 0; ks < LA; ++ks) rd(ks);
@@ -152,9 +187,10 @@ __device__ __forceinline__ void fwd_tile(const __bf16* stg, const bf16x8 (&qf)[8
     cc = 1.f;
   }
   // ---- row max and reference-max update -----------------------------------------
+  // a chain of three-input maxima: two scores per instruction
   float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
-  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
+  for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, s[0][r]), s[1][r]);
   mx = pair_max(mx);
   const float mt = (mx == -INFINITY) ? -INFINITY : mx * cc;
   const bool move = mt > m_ref + kTau;
@@ -186,17 +222,15 @@ __device__ __forceinline__ void fwd_tile(const __bf16* stg, const bf16x8 (&qf)[8
   // by two transposing reads of the row-major V tile: rows 32u + 16s2 + 4hf
   // + 0..3 and the same + 8 (the order in which the score accumulator hands
   // its keys to P's k-slots)
-  const int g16 = lane % 16, csub = (lane / 16) % 2;
-  auto at = [](int r, int cc) { return r * D + 8 * ((cc >> 3) ^ swz<C::CPR>(r)) + (cc & 7); };
 #pragma unroll
   for (int u = 0; u < 2; ++u)
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int cb = 0; cb < C::CB; ++cb) {
-        const int r0 = 32 * u + 16 * s2 + 4 * hf + g16 / 4;
-        const int c0 = 32 * cb + 16 * csub + 4 * (g16 % 4);
-        const bf16x8 va = join_tr(lds_read_tr(Vs + at(r0, c0)), lds_read_tr(Vs + at(r0 + 8, c0)));
+        const char* vr = stg + (32 * u + 16 * s2) * D * 2;
+        const bf16x8 va = join_tr(lds_read_tr(reinterpret_cast<const __bf16*>(vr + lo.v[cb][0])),
+                                  lds_read_tr(reinterpret_cast<const __bf16*>(vr + lo.v[cb][1])));
         acc[cb] = mfma32(va, pb[u][s2], acc[cb]);
       }
 }
@@ -272,22 +306,33 @@ __global__ __launch_bounds__(FwdCfg<D>::THREADS, FwdCfg<D>::WG_PER_CU) void fwd_
   float l_run = 0.f;        // this lane's share of the running sum
   const float c = a.scale_log2;
 
+  const FwdLdsOffsets<D> lo = fwd_lds_offsets<D>(lane);
   auto stage = [&](int t) { return stages + (t % C::NSTAGE) * C::STAGE; };
   for (int t = 0; t < C::AHEAD && t < ntiles; ++t) issue(kbeg + t * C::BN, stage(t));
   static_assert(C::AHEAD >= 1 && C::AHEAD <= 3, "the waits below cover up to 2 later tiles");
-  for (int t = 0; t < ntiles; ++t) {
+  static_assert(C::NSTAGE == 4, "the tile loop is unrolled over 4 stages");
+  // tile t in stage S = t % NSTAGE, S a compile-time constant
+  auto step = [&](int t, auto stage_c) {
+    constexpr int S = decltype(stage_c)::value;
     // this wave's copies of tiles t+1 .. t+AHEAD-1 may still be in flight
     const int later = min(C::AHEAD - 1, ntiles - 1 - t);
     if (C::AHEAD >= 3 && later >= 2) wait_vm<2 * C::VM>();
     else if (C::AHEAD >= 2 && later == 1) wait_vm<C::VM>();
     else wait_vm<0>();
     barrier();
-    if (t + C::AHEAD < ntiles) issue(kbeg + (t + C::AHEAD) * C::BN, stage(t + C::AHEAD));
+    if (t + C::AHEAD < ntiles) issue(kbeg + (t + C::AHEAD) * C::BN, stages + ((S + C::AHEAD) % C::NSTAGE) * C::STAGE);
     const int key0 = kbeg + t * C::BN;
     if (key0 < wave_kend) {
       const bool need_mask = (key0 + C::BN > kend) || (CAUSAL && key0 + C::BN - 1 > wave_row0 + a.diag);
-      fwd_tile<D>(stage(t), qf, acc, m_ref, l_run, c, lane, need_mask, key0, kend, row + a.diag, CAUSAL);
+      fwd_tile<D>(reinterpret_cast<const char*>(stages + S * C::STAGE), lo, qf, acc, m_ref, l_run, c, lane,
+                  need_mask, key0, kend, row + a.diag, CAUSAL);
     }
+  };
+  for (int t = 0; t < ntiles; t += C::NSTAGE) {
+    step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>{});
+    if (t + 2 < ntiles) step(t + 2, std::integral_constant<int, 2>{});
+    if (t + 3 < ntiles) step(t + 3, std::integral_constant<int, 3>{});
   }
 
   // ---- epilogue ------------------------------------------------------------------
