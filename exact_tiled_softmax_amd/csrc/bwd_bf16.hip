@@ -62,6 +62,7 @@ struct BwdArgs {
   int BH, Tq, Tk, nqb32;
   int dq_splits, dq_tiles_per_split;  // key-range split of the dQ kernel (64-key tiles per split)
   int dq_head_group;                  // heads whose query blocks the dQ kernel dispatches interleaved
+  int kv_blocks_per_wg;               // dK/dV: consecutive key blocks one workgroup walks (no causal mask)
   float scale, scale_log2;
 };
 
@@ -266,7 +267,7 @@ __device__ __forceinline__ void dkdv_grads(f32x16 (&dkt)[4], f32x16 (&dvt)[4], c
     }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool WALK>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using C = KvCfg<D>;
   __shared__ __attribute__((aligned(1024))) __bf16 stages[C::NSTAGE * C::STAGE];
@@ -275,35 +276,40 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   const int lr = lane % 32, hf = lane / 32;
+  // A workgroup owns KPW consecutive key blocks of one head (WALK, without
+  // the causal mask; else KPW = 1) and walks the query tiles of each in turn;
+  // with KPW > 1 the query-tile stream runs on across the blocks without
+  // draining.
+  static_assert(!(CAUSAL && WALK), "the key-block walk is for launches without the causal mask");
+  const int KPW = WALK ? a.kv_blocks_per_wg : 1;
   const int nkb = (a.Tk + C::BK - 1) / C::BK;
-  const int item = xcd_remap(blockIdx.x, a.BH * nkb);
-  const int kb = item % nkb;  // lowest key block (most causal work) first within a head
-  const int bh = item / nkb;
-  const int k0 = kb * C::BK;
+  const int wg_per_head = (nkb + KPW - 1) / KPW;
+  const int item = xcd_remap(blockIdx.x, a.BH * wg_per_head);
+  const int kb0 = (item % wg_per_head) * KPW;  // lowest key block (most causal work) first within a head
+  const int bh = item / wg_per_head;
+  const int nb = min(KPW, nkb - kb0);
   const int grp = wave & 3;
-  const int kw = k0 + 32 * grp;
-  const int key = kw + lr;
 
   const int nqt = (a.Tq + 31) / 32;
-  const int t_begin = CAUSAL ? min(k0 / 32, nqt) : 0;
-  const int n = nqt - t_begin;
-  // Query tiles are walked from the last one down, so that the key blocks of
-  // one head (neighbours on one XCD) stream the same tiles at about the same
-  // time and share them in L2.
-  auto tile = [&](int j) { return nqt - 1 - j; };
-  const bool grp_active = kw < a.Tk;
-  // a tile is skipped when every query of it precedes every key of the group
-  auto active = [&](int j) { return grp_active && !(CAUSAL && 32 * tile(j) + 31 < kw); };
-  auto stage = [&](int j) { return stages + (j % C::NSTAGE) * C::STAGE; };
-  auto hand = [&](int j) { return hands + (j & 1) * C::HAND + grp * C::HAND_GRP; };
+  const int t_begin = CAUSAL ? min(kb0 * C::BK / 32, nqt) : 0;
+  const int n = nqt - t_begin;  // query tiles per key block
+  const int nsteps = nb * n;
+  // Step g covers tile g % n of key block g / n.  Query tiles are walked from
+  // the last one down, so that the key blocks of one head (neighbours on one
+  // XCD) stream the same tiles at about the same time and share them in L2.
+  // (one block: g < n except for the final step, and no division is needed)
+  auto tile = [&](int g) { return nqt - 1 - (WALK ? g % n : g); };
+  auto block = [&](int g) { return WALK ? g / n : 0; };
+  auto stage = [&](int g) { return stages + (g % C::NSTAGE) * C::STAGE; };
+  auto hand = [&](int g) { return hands + (g & 1) * C::HAND + grp * C::HAND_GRP; };
 
-  // Step j (j = 0..n): tile j has landed and is published by the barrier; the
-  // copy of tile j+AHEAD goes into the stage of tile j-2; score waves work on
-  // tile j, gradient waves on tile j-1.
-  for (int j = 0; j < C::AHEAD && j < n; ++j) dkdv_issue<D>(a, bh, tile(j), stage(j), wave, lane);
-  // this wave's copies of tiles j+1 .. j+AHEAD-1 may still be in flight
-  auto wait_tile = [&](int j) {
-    const int later = min(C::AHEAD - 1, n - 1 - j);
+  // Step g (g = 0..nsteps): tile g has landed and is published by the barrier;
+  // the copy of tile g+AHEAD goes into the stage of tile g-2; score waves work
+  // on tile g, gradient waves on tile g-1.
+  for (int g = 0; g < C::AHEAD && g < nsteps; ++g) dkdv_issue<D>(a, bh, tile(g), stage(g), wave, lane);
+  // this wave's copies of tiles g+1 .. g+AHEAD-1 may still be in flight
+  auto wait_tile = [&](int g) {
+    const int later = min(C::AHEAD - 1, nsteps - 1 - g);
     if (later >= 3) wait_vm<3 * C::VM>();
     else if (later == 2) wait_vm<2 * C::VM>();
     else if (later == 1) wait_vm<C::VM>();
@@ -312,10 +318,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   static_assert(C::AHEAD == 4, "wait_tile covers up to 3 later tiles");
   if (wave < 4) {
     bf16x8 kf[8], vf[8];
-    {
+    // K and V rows of this wave's 32 keys of key block b, as B operands
+    auto load_keys = [&](int b) {
       const __bf16* Kh = a.k + (size_t)bh * a.Tk * D;
       const __bf16* Vh = a.v + (size_t)bh * a.Tk * D;
-      const int kr = min(key, a.Tk - 1);
+      const int kr = min((kb0 + b) * C::BK + 32 * grp + lr, a.Tk - 1);
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
         kf[ks] = ld16(Kh + (size_t)kr * D + 16 * ks + 8 * hf);
@@ -326,24 +333,29 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
         settle(kf[ks]);
         settle(vf[ks]);
       }
-    }
-    for (int j = 0; j <= n; ++j) {
-      wait_tile(j);
+    };
+    load_keys(0);
+    for (int g = 0; g <= nsteps; ++g) {
+      wait_tile(g);
       barrier();
-      if (j + C::AHEAD < n) dkdv_issue<D>(a, bh, tile(j + C::AHEAD), stage(j + C::AHEAD), wave, lane);
-      if (j < n) {
-        const int t = tile(j);
-        if (!active(j)) {
-          u32x4* h = reinterpret_cast<u32x4*>(hand(j)) + lane;
+      if (WALK && g < nsteps && g > 0 && g % n == 0) load_keys(g / n);  // next key block, before this step's copies
+      if (g + C::AHEAD < nsteps) dkdv_issue<D>(a, bh, tile(g + C::AHEAD), stage(g + C::AHEAD), wave, lane);
+      if (g < nsteps) {
+        const int t = tile(g);
+        const int kw = (kb0 + block(g)) * C::BK + 32 * grp;
+        // a tile is skipped when the group lies past the keys, or when every
+        // query of it precedes every key of the group
+        if (kw >= a.Tk || (CAUSAL && 32 * t + 31 < kw)) {
+          u32x4* h = reinterpret_cast<u32x4*>(hand(g)) + lane;
           const u32x4 z = {0u, 0u, 0u, 0u};
           h[0] = z;
           h[64] = z;
           h[128] = z;
           h[192] = z;
         } else if (CAUSAL && 32 * t < kw + 31) {
-          dkdv_scores<D, true>(a, kf, vf, stage(j), hand(j), t, kw, lane);
+          dkdv_scores<D, true>(a, kf, vf, stage(g), hand(g), t, kw, lane);
         } else {
-          dkdv_scores<D, false>(a, kf, vf, stage(j), hand(j), t, kw, lane);
+          dkdv_scores<D, false>(a, kf, vf, stage(g), hand(g), t, kw, lane);
         }
       }
     }
@@ -354,34 +366,51 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
       dkt[cb] = f32x16{};
       dvt[cb] = f32x16{};
     }
-    for (int j = 0; j <= n; ++j) {
-      wait_tile(j);
+    // dK = scale * (dK^T)^T, dV of key block b: register r of accumulator i is
+    // column 32cb + 8(r/4) + 4hf + r%4 of key k0 + 32 kgroup(grp, i) + lane%32
+    auto store_block = [&](int b) {
+      const int k0 = (kb0 + b) * C::BK;
+      const int cb = grp % C::CB;
+#pragma unroll
+      for (int i = 0; i < C::CB; ++i) {
+        const int kk = k0 + 32 * C::kgroup(grp, i) + lr;
+        if (kk >= a.Tk) continue;
+        __bf16* dkr = a.dk + ((size_t)bh * a.Tk + kk) * D;
+        __bf16* dvr = a.dv + ((size_t)bh * a.Tk + kk) * D;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int c = 32 * cb + 8 * g4 + 4 * hf;
+          const u32x2 wk = {pack_bf16x2(dkt[i][4 * g4] * a.scale, dkt[i][4 * g4 + 1] * a.scale),
+                            pack_bf16x2(dkt[i][4 * g4 + 2] * a.scale, dkt[i][4 * g4 + 3] * a.scale)};
+          const u32x2 wv = {pack_bf16x2(dvt[i][4 * g4], dvt[i][4 * g4 + 1]),
+                            pack_bf16x2(dvt[i][4 * g4 + 2], dvt[i][4 * g4 + 3])};
+          *reinterpret_cast<u32x2*>(dkr + c) = wk;
+          *reinterpret_cast<u32x2*>(dvr + c) = wv;
+        }
+      }
+    };
+    for (int g = 0; g <= nsteps; ++g) {
+      wait_tile(g);
       barrier();
-      if (j + C::AHEAD < n) dkdv_issue<D>(a, bh, tile(j + C::AHEAD), stage(j + C::AHEAD), wave, lane);
+      if (g + C::AHEAD < nsteps) dkdv_issue<D>(a, bh, tile(g + C::AHEAD), stage(g + C::AHEAD), wave, lane);
       // every tile in range has an active key group (the first one); score
       // waves of inactive groups hand over zeros
-      if (j >= 1) dkdv_grads<D>(dkt, dvt, stage(j - 1), hands + ((j - 1) & 1) * C::HAND, grp, lane);
-    }
-    // dK = scale * (dK^T)^T, dV: register r of accumulator i is column
-    // 32cb + 8(r/4) + 4hf + r%4 of key k0 + 32 kgroup(grp, i) + lane%32
-    const int cb = grp % C::CB;
+      if (g >= 1) {
+        dkdv_grads<D>(dkt, dvt, stage(g - 1), hands + ((g - 1) & 1) * C::HAND, grp, lane);
+        if (WALK && g % n == 0 && g < nsteps) {
+          // tile g-1 closed key block g/n - 1: write it, start the next
+          store_block(g / n - 1);
 #pragma unroll
-    for (int i = 0; i < C::CB; ++i) {
-      const int kk = k0 + 32 * C::kgroup(grp, i) + lr;
-      if (kk >= a.Tk) continue;
-      __bf16* dkr = a.dk + ((size_t)bh * a.Tk + kk) * D;
-      __bf16* dvr = a.dv + ((size_t)bh * a.Tk + kk) * D;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int c = 32 * cb + 8 * g + 4 * hf;
-        const u32x2 wk = {pack_bf16x2(dkt[i][4 * g] * a.scale, dkt[i][4 * g + 1] * a.scale),
-                          pack_bf16x2(dkt[i][4 * g + 2] * a.scale, dkt[i][4 * g + 3] * a.scale)};
-        const u32x2 wv = {pack_bf16x2(dvt[i][4 * g], dvt[i][4 * g + 1]),
-                          pack_bf16x2(dvt[i][4 * g + 2], dvt[i][4 * g + 3])};
-        *reinterpret_cast<u32x2*>(dkr + c) = wk;
-        *reinterpret_cast<u32x2*>(dvr + c) = wv;
+          for (int cb = 0; cb < C::CB; ++cb) {
+            dkt[cb] = f32x16{};
+            dvt[cb] = f32x16{};
+          }
+        }
       }
     }
+    // the last (or only) block; zeros when no query reaches it (causal keys
+    // past every query)
+    store_block(nb - 1);
   }
 }
 
@@ -668,6 +697,22 @@ BwdLayout bwd_layout(int BH, int Tq, int Tk, int d, int dq_splits) {
   return L;
 }
 
+// Key blocks per dK/dV workgroup without the causal mask: with very few query
+// tiles (at most 8, Tq <= 256) a workgroup's fill and drain (K/V rows loaded,
+// the query-tile stream started, dK/dV written) weigh on its few steps, so one
+// workgroup walks several consecutive key blocks of a head (about 128
+// query-tile steps), as long as the launch keeps at least two workgroups per
+// CU.  (Measured: Tq=256 Tk=65536 backward 2.84 vs 2.98 ms; with 64 query
+// tiles a 2-block walk was 9% slower, so longer query ranges keep one block.)
+int dkdv_blocks_per_wg(int BH, int Tq, int nkb) {
+  const int nqt = (Tq + 31) / 32;
+  if (nqt > 8) return 1;
+  int kpw = std::max(1, 128 / nqt);
+  kpw = std::min(kpw, nkb);
+  while (kpw > 1 && (long long)BH * ((nkb + kpw - 1) / kpw) < 512) kpw /= 2;
+  return kpw;
+}
+
 template <int D>
 hipError_t bwd_launch_d(BwdArgs& args, const __bf16* o, const float* lse, const float* dlse, bool causal, char* ws,
                         const BwdLayout& L, hipStream_t stream) {
@@ -685,11 +730,15 @@ hipError_t bwd_launch_d(BwdArgs& args, const __bf16* o, const float* lse, const 
   if (e != hipSuccess) return e;
 
   const int nkb = (args.Tk + KvCfg<D>::BK - 1) / KvCfg<D>::BK;
+  args.kv_blocks_per_wg = causal ? 1 : dkdv_blocks_per_wg(args.BH, args.Tq, nkb);
+  const int wg_per_head = (nkb + args.kv_blocks_per_wg - 1) / args.kv_blocks_per_wg;
   prof_begin(3, stream);
   if (causal)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(args.BH * nkb), dim3(512), 0, stream, args);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, false>), dim3(args.BH * nkb), dim3(512), 0, stream, args);
+  else if (args.kv_blocks_per_wg > 1)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, true>), dim3(args.BH * wg_per_head), dim3(512), 0, stream, args);
   else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(args.BH * nkb), dim3(512), 0, stream, args);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, false>), dim3(args.BH * nkb), dim3(512), 0, stream, args);
   prof_end(3, stream);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -288,3 +288,23 @@ def test_bf16_scale_zero_gives_mean_of_allowed_values(dev):
     ro, rl = dense_forward(f64(q), f64(k), f64(v), 0.0, True)
     assert_close("O", f64(o), ro, TOL_BF16)
     assert_close("LSE", f64(lse), rl, TOL_LSE_BF16)
+
+
+# Without the causal mask and with few query tiles, one dK/dV workgroup walks
+# several consecutive key blocks of a head (the query-tile stream runs on
+# across them).  64 heads keep the launch large enough for the walk to be
+# chosen; ragged key counts leave a short last block and a workgroup with
+# fewer blocks than the others.
+@pytest.mark.parametrize("shape", [(1, 64, 64, 2048, 128, 128),   # 2 key blocks per workgroup
+                                   (1, 128, 40, 1700, 128, 128),  # 3 per workgroup, the last one 2, last block 36 keys
+                                   (2, 64, 33, 1000, 64, 64)])    # 2 per workgroup, last block 104 keys
+def test_bf16_bwd_key_block_walk(dev, shape):
+    q, k, v, do = bf16_problem(shape, seed=13)
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    o, lse = attn.fwd(qd, kd, vd, causal=False)
+    dq, dk, dv = attn.bwd(qd, kd, vd, o, lse, dod, causal=False)
+    torch.cuda.synchronize()
+    rq, rk, rv = dense_backward(f64(q), f64(k), f64(v), f64(do), 1 / np.sqrt(shape[4]), False)
+    assert_close("dQ", f64(dq), rq, TOL_BF16)
+    assert_close("dK", f64(dk), rk, TOL_BF16)
+    assert_close("dV", f64(dv), rv, TOL_BF16)
