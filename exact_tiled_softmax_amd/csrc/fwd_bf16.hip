@@ -27,11 +27,15 @@
 //
 // The reference max m used in the exponent is only moved when a row's tile
 // max exceeds it by more than kTau (log2 units); then l and a are rescaled by
-// exp2(m_old - m_new) as in the page's recurrence.  Between moves P <= 2^kTau,
-// and O = a / l and LSE = m + log2 l are the same quantities for any m (the
-// result is exact; only fp32 rounding differs).  This keeps the 64-register
-// rescale of a off the common path.  A row with no allowed key yet keeps
-// m = -inf and uses 0 in its exponent (the page's guard).
+// exp2(m_old - m_new) as in the page's recurrence.  O = a / l and LSE = m +
+// log2 l are the same quantities for any m (the result is exact; only fp32
+// rounding differs), so m only has to keep P bounded.  An unmasked tile
+// (head dim 128) therefore takes no row max at all: its P is computed against
+// the current m and kept when the tile's row sum is at most 2^16 (every
+// value of P at most 2^16); only past that bound is the tile redone with its
+// row max.  This keeps both the row max and the 64-register rescale of a off
+// the common path.  A row with no allowed key yet keeps m = -inf and uses 0
+// in its exponent (the page's guard).
 //
 // With key splits, each workgroup covers one contiguous key range and stores
 // its unnormalised state (m, l, a) in fp32; a second kernel merges the states
@@ -47,6 +51,9 @@ namespace attn {
 namespace {
 
 constexpr float kTau = 8.f;  // lazy-rescale threshold (log2 units)
+// largest row sum of one tile's P accepted without a row max (every value of
+// P is then at most 2^16)
+constexpr float kFastSum = 65536.f;
 
 template <int D>
 struct FwdCfg {
@@ -174,48 +181,63 @@ __device__ __forceinline__ void fwd_tile(const char* stg, const FwdLdsOffsets<D>
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // accumulator register r of block u: key key0 + 32u + 8(r/4) + 4hf + r%4
-  float cc = c;
-  if (need_mask) {
+  // ---- P (bf16 B operand: k-slot 8hf+e of step s2 = register 8*s2 + e) ------------
+  float psum = 0.f;
+  bf16x8 pb[2][2];
+  auto make_p = [&](float cc, float mu) {
+    psum = 0.f;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = key0 + 32 * u + 8 * (r / 4) + 4 * hf + (r % 4);
-        s[u][r] = (key >= kend || (causal && key > row)) ? -INFINITY : s[u][r] * c;  // row: i + diag
+        const float x = fast_exp2(__builtin_fmaf(s[u][r], cc, -mu));
+        psum += x;
+        pb[u][r / 8][r % 8] = to_bf16(x);
       }
-    cc = 1.f;
+  };
+  // Fast path (head dim 128, an unmasked tile, every row with a finite
+  // reference): P against the current reference without a row max; the row
+  // sum shows whether any value has grown past the bound, and only then the
+  // tile is redone with the row max.  (At head dim 64 the branch costs more
+  // than the maxima it saves.)
+  bool redo = true;
+  if (D == 128 && !need_mask && !__builtin_amdgcn_ballot_w64(m_ref == -INFINITY)) {
+    make_p(c, m_ref);
+    redo = __builtin_amdgcn_ballot_w64(!(psum <= kFastSum)) != 0;
   }
-  // ---- row max and reference-max update -----------------------------------------
-  // a chain of three-input maxima: two scores per instruction
-  float mx = fmaxf(s[0][0], s[1][0]);
+  if (redo) {
+    // accumulator register r of block u: key key0 + 32u + 8(r/4) + 4hf + r%4
+    float cc = c;
+    if (need_mask) {
 #pragma unroll
-  for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, s[0][r]), s[1][r]);
-  mx = pair_max(mx);
-  const float mt = (mx == -INFINITY) ? -INFINITY : mx * cc;
-  const bool move = mt > m_ref + kTau;
-  if (__builtin_amdgcn_ballot_w64(move)) {
-    const float m_new = move ? mt : m_ref;
-    const float alpha = move ? fast_exp2(m_ref - m_new) : 1.f;  // m_ref = -inf -> 0
-    l_run *= alpha;
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int cb = 0; cb < C::CB; ++cb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[cb][r] *= alpha;
-    m_ref = m_new;
-  }
-  const float mu = (m_ref == -INFINITY) ? 0.f : m_ref;
-  // ---- P (bf16 B operand: k-slot 8hf+e of step s2 = register 8*s2 + e) ------------
-  float psum = 0.f;
-  bf16x8 pb[2][2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float x = fast_exp2(__builtin_fmaf(s[u][r], cc, -mu));
-      psum += x;
-      pb[u][r / 8][r % 8] = to_bf16(x);
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 32 * u + 8 * (r / 4) + 4 * hf + (r % 4);
+          s[u][r] = (key >= kend || (causal && key > row)) ? -INFINITY : s[u][r] * c;  // row: i + diag
+        }
+      cc = 1.f;
     }
+    // ---- row max and reference-max update ---------------------------------------
+    // a chain of three-input maxima: two scores per instruction
+    float mx = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, s[0][r]), s[1][r]);
+    mx = pair_max(mx);
+    const float mt = (mx == -INFINITY) ? -INFINITY : mx * cc;
+    const bool move = mt > m_ref + kTau;
+    if (__builtin_amdgcn_ballot_w64(move)) {
+      const float m_new = move ? mt : m_ref;
+      const float alpha = move ? fast_exp2(m_ref - m_new) : 1.f;  // m_ref = -inf -> 0
+      l_run *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[cb][r] *= alpha;
+      m_ref = m_new;
+    }
+    make_p(cc, (m_ref == -INFINITY) ? 0.f : m_ref);
+  }
   l_run += psum;
   // ---- a += V^T P^T -----------------------------------------------------------------
   // A operand (column 32cb + lane%32 of V, k-slots = the keys of P's k-slots)

@@ -240,6 +240,30 @@ def test_bf16_fwd_large_scores(dev, sigma_q, causal):
     assert_close("LSE", f64(lse), rl, TOL_LSE_BF16)
 
 
+# Scores that keep rising along the keys (key rows scaled by 1 + 7 j / Tk),
+# so that a later unmasked tile overshoots the reference max set by an
+# earlier one by far more than the 2^16 that a tile's P may reach without a
+# row max: those tiles are redone with their row max and the state rescaled.
+# The reverse order (falling scores) keeps the first reference throughout.
+@pytest.mark.parametrize("rising", [True, False])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_fwd_drifting_scores(dev, rising, causal):
+    shape = (1, 2, 520, 1500, 128, 128)
+    B, H, Tq, Tk, d, dv = shape
+    q, k, v, _ = random_problem(21, B, H, Tq, Tk, d, dv, "f32", sigma_q=3.0)
+    ramp = 1.0 + 7.0 * np.arange(Tk, dtype=np.float32) / Tk
+    if not rising:
+        ramp = ramp[::-1].copy()
+    k = k * torch.from_numpy(ramp)[None, None, :, None]
+    q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    o, lse = attn.fwd(q.to(dev), k.to(dev), v.to(dev), causal=causal)
+    torch.cuda.synchronize()
+    ro, rl = dense_forward(f64(q), f64(k), f64(v), 1 / np.sqrt(d), causal)
+    assert np.all(np.isfinite(f64(o))) and np.all(np.isfinite(f64(lse)))
+    assert_close("O", f64(o), ro, TOL_BF16)
+    assert_close("LSE", f64(lse), rl, TOL_LSE_BF16)
+
+
 # The backward at large scores (near one-hot rows, where the exact dS cancels):
 # D comes from the forward's bf16 O and dS is rounded to bf16 before dK =
 # scale dS^T Q, which multiplies its error by |Q|.  Elements are accepted
