@@ -120,7 +120,9 @@ __global__ __launch_bounds__(256) void bwd_stats_kernel(const __bf16* __restrict
 //     Q^T dS, reading its column block of dO and Q with transposing LDS reads
 //     (shared by all its key groups) and P, dS from the score waves.
 // The partner's MFMA work fills the SIMD while the score wave does its
-// softmax, and neither role needs more than half the register file.
+// softmax, and neither role needs more than half the register file.  The
+// score waves' chain sets the step time, so the gradient waves (which wait
+// at the barrier for them) issue every tile copy.
 template <int D>
 struct KvCfg {
   static constexpr int KS = D / 16;                    // 16-wide k-steps over d
@@ -130,8 +132,8 @@ struct KvCfg {
   static constexpr int BK = 128;                       // keys per workgroup
   static constexpr int TILE = 32 * D;                  // bf16 elements of one Q or dO tile
   static constexpr int PER_TENSOR = TILE * 2 / 1024;   // wave copies per tensor and tile
-  static constexpr int PER_WAVE = 2 * PER_TENSOR / WAVES;
-  static constexpr int VM = PER_WAVE + 1;              // vector-memory ops per wave and tile (+ stats)
+  static constexpr int PER_WAVE = 2 * PER_TENSOR / 4;  // copies per gradient wave (they issue all copies)
+  static constexpr int VM = PER_WAVE + 1;              // vector-memory ops per gradient wave and tile (+ stats)
   static constexpr int STAGE = 2 * TILE + 128;         // bf16 elements per stage (stats: 64 floats)
   static constexpr int NSTAGE = 6;                     // tiles j-1 .. j+4 resident
   static constexpr int AHEAD = NSTAGE - 2;             // copies in flight ahead of the score waves
@@ -140,27 +142,29 @@ struct KvCfg {
   // gradient wave gw (0..3) owns column block gw % CB of d and key groups
   // kgroup(gw, 0..CB-1): the 4 * CB (block, group) pairs, CB per wave
   __host__ __device__ static constexpr int kgroup(int gw, int i) { return gw / CB + (4 / CB) * i; }
-  static_assert(PER_WAVE >= 1 && 2 * PER_TENSOR == PER_WAVE * WAVES, "tile copy split");
+  static_assert(PER_WAVE >= 1 && 2 * PER_TENSOR == PER_WAVE * 4, "tile copy split");
 };
 
+// The gradient waves (gw = 0..3) issue every copy of a tile: the score
+// waves, whose chain sets the step time, issue none.
 template <int D>
-__device__ __forceinline__ void dkdv_issue(const BwdArgs& a, int bh, int t, __bf16* stg, int wave, int lane) {
+__device__ __forceinline__ void dkdv_issue(const BwdArgs& a, int bh, int t, __bf16* stg, int gw, int lane) {
   using C = KvCfg<D>;
   const __bf16* Qh = a.q + (size_t)bh * a.Tq * D;
   const __bf16* dOh = a.dout + (size_t)bh * a.Tq * D;
 #pragma unroll
   for (int n = 0; n < C::PER_WAVE; ++n) {
-    const int cpy = wave * C::PER_WAVE + n;  // wave-uniform
+    const int cpy = gw * C::PER_WAVE + n;  // wave-uniform
     const int tensor = cpy / C::PER_TENSOR, i = cpy % C::PER_TENSOR;
     const int p = 64 * i + lane;
     const int row = p / C::CPR, c = (p % C::CPR) ^ swz<C::CPR>(row);
     const int qq = min(32 * t + row, a.Tq - 1);
     dma16((tensor == 0 ? Qh : dOh) + (size_t)qq * D + 8 * c, stg + tensor * C::TILE + 512 * i);
   }
-  // 256 bytes of row statistics: lanes 0..1 of every wave copy 32 of them
-  if (lane < 2) {
-    const float* src = a.stats + ((size_t)bh * a.nqb32 + t) * 64 + 8 * wave + 4 * lane;
-    dma16(reinterpret_cast<const __bf16*>(src), stg + 2 * C::TILE + 16 * wave);
+  // 256 bytes of row statistics: lanes 0..3 of every gradient wave copy 64 of them
+  if (lane < 4) {
+    const float* src = a.stats + ((size_t)bh * a.nqb32 + t) * 64 + 16 * gw + 4 * lane;
+    dma16(reinterpret_cast<const __bf16*>(src), stg + 2 * C::TILE + 32 * gw);
   }
 }
 
@@ -306,8 +310,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // Step g (g = 0..nsteps): tile g has landed and is published by the barrier;
   // the copy of tile g+AHEAD goes into the stage of tile g-2; score waves work
   // on tile g, gradient waves on tile g-1.
-  for (int g = 0; g < C::AHEAD && g < nsteps; ++g) dkdv_issue<D>(a, bh, tile(g), stage(g), wave, lane);
-  // this wave's copies of tiles g+1 .. g+AHEAD-1 may still be in flight
+  if (wave >= 4)
+    for (int g = 0; g < C::AHEAD && g < nsteps; ++g) dkdv_issue<D>(a, bh, tile(g), stage(g), grp, lane);
+  // a gradient wave's copies of tiles g+1 .. g+AHEAD-1 may still be in flight
   auto wait_tile = [&](int g) {
     const int later = min(C::AHEAD - 1, nsteps - 1 - g);
     if (later >= 3) wait_vm<3 * C::VM>();
@@ -336,10 +341,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
     };
     load_keys(0);
     for (int g = 0; g <= nsteps; ++g) {
-      wait_tile(g);
       barrier();
-      if (WALK && g < nsteps && g > 0 && g % n == 0) load_keys(g / n);  // next key block, before this step's copies
-      if (g + C::AHEAD < nsteps) dkdv_issue<D>(a, bh, tile(g + C::AHEAD), stage(g + C::AHEAD), wave, lane);
+      if (WALK && g < nsteps && g > 0 && g % n == 0) load_keys(g / n);  // next key block
       if (g < nsteps) {
         const int t = tile(g);
         const int kw = (kb0 + block(g)) * C::BK + 32 * grp;
@@ -392,7 +395,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
     for (int g = 0; g <= nsteps; ++g) {
       wait_tile(g);
       barrier();
-      if (g + C::AHEAD < nsteps) dkdv_issue<D>(a, bh, tile(g + C::AHEAD), stage(g + C::AHEAD), wave, lane);
+      if (g + C::AHEAD < nsteps) dkdv_issue<D>(a, bh, tile(g + C::AHEAD), stage(g + C::AHEAD), grp, lane);
       // every tile in range has an active key group (the first one); score
       // waves of inactive groups hand over zeros
       if (g >= 1) {
