@@ -135,7 +135,10 @@ struct KvCfg {
   static constexpr int PER_WAVE = 2 * PER_TENSOR / 4;  // copies per gradient wave (they issue all copies)
   static constexpr int VM = PER_WAVE + 1;              // vector-memory ops per gradient wave and tile (+ stats)
   static constexpr int STAGE = 2 * TILE + 128;         // bf16 elements per stage (stats: 64 floats)
-  static constexpr int NSTAGE = 6;                     // tiles j-1 .. j+4 resident
+  // Tiles j-1 .. j+2 resident, copies two tiles ahead.  With four tiles in
+  // flight (six stages) the gradient waves' copy issue stalled behind the
+  // copies still outstanding and the backward was 3-13% slower.
+  static constexpr int NSTAGE = 4;
   static constexpr int AHEAD = NSTAGE - 2;             // copies in flight ahead of the score waves
   static constexpr int HAND_GRP = 64 * 4 * 8;          // bf16 elements of one group's P/dS hand-off (64 lanes x 4 x 8)
   static constexpr int HAND = 4 * HAND_GRP;            // all 4 key groups
@@ -320,7 +323,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
     else if (later == 1) wait_vm<C::VM>();
     else wait_vm<0>();
   };
-  static_assert(C::AHEAD == 4, "wait_tile covers up to 3 later tiles");
+  static_assert(C::AHEAD >= 1 && C::AHEAD <= 4, "wait_tile covers up to 3 later tiles");
   if (wave < 4) {
     bf16x8 kf[8], vf[8];
     // K and V rows of this wave's 32 keys of key block b, as B operands
