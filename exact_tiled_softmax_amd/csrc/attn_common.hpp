@@ -73,6 +73,11 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
 
+// Word 3 of a raw buffer resource on gfx9 (data format 32, no swizzle, no
+// index stride): a buffer access past the record size the resource gives is
+// dropped (stores) or reads zero (loads) instead of touching memory.
+constexpr int kBufferWord3 = 0x00020000;
+
 // Byte permute: result byte i = byte sel[i] of the 8-byte value {hi:lo}.
 __device__ __forceinline__ unsigned perm_b32(unsigned hi, unsigned lo, unsigned sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);

@@ -14,18 +14,21 @@
 // keys), so they come from two kernels that each keep their own accumulator
 // in registers and write it once; no workgroup adds into another's output.
 // Kernels, in launch order:
-//   bwd_stats      per query row: LSE * log2(e) (+inf for a row that is
-//                  outside Tq or has no allowed key, so its P is 0) and
-//                  D = sum_c dO_c O_c, blocked 32 rows at a time.  With an
+//   bwd_stats      per query row: LSE * log2(e) and -LSE / scale (+inf and
+//                  -inf for a row that is outside Tq or has no allowed key,
+//                  so its P is 0) and -D, D = sum_c dO_c O_c, blocked 32 rows
+//                  at a time.  With an
 //                  upstream gradient dLSE on the log-sum-exp, dS gains
 //                  dLSE_i P_ij (the row sum l is a smooth function of the
 //                  inputs that gradients flow through: "The Hidden Recurrence
 //                  in Softmax Attention", sections "Flash Attention Backward
 //                  Pass" and "Gradient at the Output"), i.e. D becomes D - dLSE.
-//   bwd_dkdv       one workgroup (8 waves) per 128 keys, walking 32-query
-//                  tiles streamed into LDS (see the kernel's comment):
-//                    S = Q K^T, dP = dO V^T, P = exp2(S*scale*log2e - LSE2),
-//                    dS = P o (dP - D), dV^T += dO^T P, dK^T += Q^T dS
+//   bwd_dkdv       persistent: each workgroup (8 waves) runs a fixed list of
+//                  128-key blocks back to back, walking 32-query tiles
+//                  streamed into LDS (see the kernel's comment):
+//                    S' = Q K^T - LSE/scale, dP' = dO V^T - D (both from the
+//                    MFMA accumulators' start values), P = exp2(S'*scale*log2e),
+//                    dS = P o dP', dV^T += dO^T P, dK^T += Q^T dS
 //   bwd_dq         one workgroup (8 waves) per 256 queries; each wave keeps
 //                  its 32 queries' Q and dO rows as MFMA operands and dQ^T in
 //                  registers and walks 64-key tiles streamed into LDS:
@@ -37,6 +40,7 @@
 // tiles are copied global -> LDS by the direct-to-LDS vector load, several
 // tiles ahead of the compute.
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 
 #include "attn.h"
@@ -49,12 +53,17 @@ namespace attn {
 
 namespace {
 
+// Row statistics of one 32-row block: LSE * log2(e) (the dQ kernel's
+// exponent offset), -LSE / scale and -D (the dK/dV kernel's accumulator
+// start values, so that its MFMAs produce S - LSE/scale and dP - D).
+constexpr int kStatsPerBlock = 96;
+
 struct BwdArgs {
   const __bf16* q;
   const __bf16* k;
   const __bf16* v;
   const __bf16* dout;
-  const float* stats;  // [BH][nqb32][64]: lse2 x32, D x32 per 32-row block
+  const float* stats;  // [BH][nqb32][kStatsPerBlock] per 32-row block: LSE*log2(e) x32, -LSE/scale x32, -D x32
   __bf16* dq;
   __bf16* dk;
   __bf16* dv;
@@ -62,7 +71,8 @@ struct BwdArgs {
   int BH, Tq, Tk, nqb32;
   int dq_splits, dq_tiles_per_split;  // key-range split of the dQ kernel (64-key tiles per split)
   int dq_head_group;                  // heads whose query blocks the dQ kernel dispatches interleaved
-  int kv_blocks_per_wg;               // dK/dV: consecutive key blocks one workgroup walks (no causal mask)
+  int kv_nwg, kv_nkb;                 // dK/dV: workgroups of the persistent launch, 128-key blocks per head
+  int kv_zero_items;                  // dK/dV (causal): some key blocks are past every query
   float scale, scale_log2;
 };
 
@@ -73,7 +83,8 @@ struct BwdArgs {
 template <int D>
 __global__ __launch_bounds__(256) void bwd_stats_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ dout,
                                                         const float* __restrict__ lse, const float* __restrict__ dlse,
-                                                        float* __restrict__ stats, int BH, int Tq, int nqb32) {
+                                                        float* __restrict__ stats, int BH, int Tq, int nqb32,
+                                                        float scale) {
   constexpr int PER = D / 16;
   const int sub = threadIdx.x % 16;
   const size_t rows_pad = (size_t)nqb32 * 32;
@@ -96,21 +107,24 @@ __global__ __launch_bounds__(256) void bwd_stats_kernel(const __bf16* __restrict
 #pragma unroll
     for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
     if (sub == 0) {
-      float l2 = INFINITY;
+      float l2 = INFINITY, nl = -INFINITY;
       if (ok) {
         const float l = lse[bh * Tq + qi];
         l2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
+        nl = (l == -INFINITY) ? -INFINITY : -l / scale;
       }
-      float* blk = stats + (bh * nqb32 + qi / 32) * 64;
+      float* blk = stats + (bh * nqb32 + qi / 32) * kStatsPerBlock;
       blk[qi % 32] = l2;
-      blk[32 + qi % 32] = ok ? acc - (dlse ? dlse[bh * Tq + qi] : 0.f) : 0.f;
+      blk[32 + qi % 32] = nl;
+      blk[64 + qi % 32] = ok ? (dlse ? dlse[bh * Tq + qi] : 0.f) - acc : 0.f;
     }
   }
 }
 
 // ---------------------------------------------------------------------------------
-// bwd_dkdv: one workgroup of 8 waves per 128 keys.  Waves w and w+4 run on the
-// same SIMD and share key group w (32 keys):
+// bwd_dkdv: workgroups of 8 waves, each owning 128 keys (an item) at a time
+// and running its list of items back to back (KvItem below).  Waves w and w+4
+// run on the same SIMD and share key group w (32 keys):
 //   score wave (w < 4): holds its keys' K and V rows as MFMA operands; per
 //     32-query tile computes S = Q K^T, dP = dO V^T, P and dS and hands P, dS
 //     (bf16 MFMA operands, in the lane layout both waves use) to its partner
@@ -123,18 +137,20 @@ __global__ __launch_bounds__(256) void bwd_stats_kernel(const __bf16* __restrict
 // softmax, and neither role needs more than half the register file.  The
 // score waves' chain sets the step time, so the gradient waves (which wait
 // at the barrier for them) issue every tile copy.
+constexpr int kKvBlock = 128;  // keys of one dK/dV item
+
 template <int D>
 struct KvCfg {
   static constexpr int KS = D / 16;                    // 16-wide k-steps over d
   static constexpr int CB = D / 32;                    // 32-row blocks of d
   static constexpr int CPR = D / 8;                    // 16-byte chunks per Q / dO row
   static constexpr int WAVES = 8;
-  static constexpr int BK = 128;                       // keys per workgroup
+  static constexpr int BK = kKvBlock;                  // keys per item (one workgroup's accumulators)
   static constexpr int TILE = 32 * D;                  // bf16 elements of one Q or dO tile
   static constexpr int PER_TENSOR = TILE * 2 / 1024;   // wave copies per tensor and tile
   static constexpr int PER_WAVE = 2 * PER_TENSOR / 4;  // copies per gradient wave (they issue all copies)
   static constexpr int VM = PER_WAVE + 1;              // vector-memory ops per gradient wave and tile (+ stats)
-  static constexpr int STAGE = 2 * TILE + 128;         // bf16 elements per stage (stats: 64 floats)
+  static constexpr int STAGE = 2 * TILE + 128;         // bf16 elements per stage (-LSE/scale, -D: 64 floats)
   // Tiles j-1 .. j+2 resident, copies two tiles ahead.  With four tiles in
   // flight (six stages) the gradient waves' copy issue stalled behind the
   // copies still outstanding and the backward was 3-13% slower.
@@ -149,32 +165,41 @@ struct KvCfg {
 };
 
 // The gradient waves (gw = 0..3) issue every copy of a tile: the score
-// waves, whose chain sets the step time, issue none.
+// waves, whose chain sets the step time, issue none.  Each copy takes a
+// wave-uniform base (the tile's first row, in scalar registers) and a 32-bit
+// per-lane byte offset; rows past Tq repeat the last query row.
 template <int D>
 __device__ __forceinline__ void dkdv_issue(const BwdArgs& a, int bh, int t, __bf16* stg, int gw, int lane) {
   using C = KvCfg<D>;
-  const __bf16* Qh = a.q + (size_t)bh * a.Tq * D;
-  const __bf16* dOh = a.dout + (size_t)bh * a.Tq * D;
+  const size_t row0 = (size_t)bh * a.Tq + 32 * t;
+  const __bf16* Qt = a.q + row0 * D;
+  const __bf16* dOt = a.dout + row0 * D;
+  const int last = a.Tq - 1 - 32 * t;  // last row of the tile inside Tq (>= 0)
 #pragma unroll
   for (int n = 0; n < C::PER_WAVE; ++n) {
     const int cpy = gw * C::PER_WAVE + n;  // wave-uniform
     const int tensor = cpy / C::PER_TENSOR, i = cpy % C::PER_TENSOR;
     const int p = 64 * i + lane;
     const int row = p / C::CPR, c = (p % C::CPR) ^ swz<C::CPR>(row);
-    const int qq = min(32 * t + row, a.Tq - 1);
-    dma16((tensor == 0 ? Qh : dOh) + (size_t)qq * D + 8 * c, stg + tensor * C::TILE + 512 * i);
+    const uint32_t off = (uint32_t)(min(row, last) * D + 8 * c) * 2;
+    dma16_sbase(tensor == 0 ? Qt : dOt, off, stg + tensor * C::TILE + 512 * i);
   }
-  // 256 bytes of row statistics: lanes 0..3 of every gradient wave copy 64 of them
+  // 256 bytes of row statistics (-LSE/scale, -D): lanes 0..3 of every
+  // gradient wave copy 64 of them
   if (lane < 4) {
-    const float* src = a.stats + ((size_t)bh * a.nqb32 + t) * 64 + 16 * gw + 4 * lane;
-    dma16(reinterpret_cast<const __bf16*>(src), stg + 2 * C::TILE + 32 * gw);
+    const float* src = a.stats + ((size_t)bh * a.nqb32 + t) * kStatsPerBlock + 32 + 16 * gw;
+    dma16_sbase(src, (uint32_t)(16 * lane), stg + 2 * C::TILE + 32 * gw);
   }
 }
 
 // Score wave, one tile: P and dS as bf16 B operands (k-slot 8hf+e of k-step
-// s2 = accumulator register 8*s2 + e), stored per lane into `hand`.
+// s2 = accumulator register 8*s2 + e), stored per lane into `hand`.  The
+// accumulators start at -LSE/scale and -D of their rows, so the MFMAs leave
+// S - LSE/scale and dP - D: P = exp2(scale*log2(e) * that) and dS = P (dP - D).
+// MASK (a tile on the causal diagonal): S starts at -inf where the key
+// follows the query, which makes P and dS zero there.
 template <int D, bool MASK>
-__device__ __forceinline__ void dkdv_scores(const BwdArgs& a, const bf16x8 (&kf)[8], const bf16x8 (&vf)[8],
+__device__ __forceinline__ void dkdv_scores(const BwdArgs& a, const bf16x8 (&kf)[KvCfg<D>::KS], const bf16x8 (&vf)[KvCfg<D>::KS],
                                             const __bf16* stg, __bf16* hand, int t, int kw, int lane) {
   using C = KvCfg<D>;
   const int lr = lane % 32, hf = lane / 32;
@@ -186,23 +211,28 @@ __device__ __forceinline__ void dkdv_scores(const BwdArgs& a, const bf16x8 (&kf)
   // every LDS read of the tile is issued before the first MFMA, so their
   // latencies overlap instead of adding up
   bf16x8 qa[C::KS], da[C::KS];
-  f32x4 l4[4], d4[4];
+  f32x16 s, dp;
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) {
     const int off = lr * D + 8 * ((2 * ks + hf) ^ rsw);
     qa[ks] = ld16(Qs + off);
     da[ks] = ld16(dOs + off);
   }
+  // accumulator register r = 4g + i: row 8g + 4hf + i of the tile
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    l4[g] = *reinterpret_cast<const f32x4*>(sts + 8 * g + 4 * hf);
-    d4[g] = *reinterpret_cast<const f32x4*>(sts + 32 + 8 * g + 4 * hf);
+    const f32x4 l4 = *reinterpret_cast<const f32x4*>(sts + 8 * g + 4 * hf);
+    const f32x4 d4 = *reinterpret_cast<const f32x4*>(sts + 32 + 8 * g + 4 * hf);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s[4 * g + i] = (MASK && key > 32 * t + 8 * g + 4 * hf + i) ? -INFINITY : l4[i];
+      dp[4 * g + i] = d4[i];
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
   // the score wave goes first on the SIMD's matrix unit; its partner's MFMAs
   // then run while it does the softmax
   __builtin_amdgcn_s_setprio(2);
-  f32x16 s = {}, dp = {};
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) {
     s = mfma32(qa[ks], kf[ks], s);
@@ -217,10 +247,9 @@ __device__ __forceinline__ void dkdv_scores(const BwdArgs& a, const bf16x8 (&kf)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * g + i;
-      float p = fast_exp2(__builtin_fmaf(s[r], a.scale_log2, -l4[g][i]));
-      if (MASK) p = (key > 32 * t + 8 * g + 4 * hf + i) ? 0.f : p;
+      const float p = fast_exp2(s[r] * a.scale_log2);
       pb[r / 8][r % 8] = to_bf16(p);
-      db[r / 8][r % 8] = to_bf16(p * (dp[r] - d4[g][i]));
+      db[r / 8][r % 8] = to_bf16(p * dp[r]);
     }
   }
   u32x4* h = reinterpret_cast<u32x4*>(hand) + lane;
@@ -274,8 +303,118 @@ __device__ __forceinline__ void dkdv_grads(f32x16 (&dkt)[4], f32x16 (&dvt)[4], c
     }
 }
 
-template <int D, bool CAUSAL, bool WALK>
-__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
+// Work list of the dK/dV launch.  The launch is persistent: kv_nwg
+// workgroups (as many as are resident on the chip at once) each run a fixed
+// list of items (head, key block) back to back as one stream of query tiles,
+// each item walked from its last query tile down.  No workgroup waits on the
+// dispatcher between items (with one workgroup per CU a finished workgroup's
+// CU idled about 6 us, median, before the next one started), and the tile
+// copies, key loads and gradient stores of consecutive items overlap.
+//   causal mask: item pairs (key block k, key block nkb-1-k) of one head, whose
+//     tile counts add up to the same total for every k when Tq = Tk, dealt
+//     round-robin over the workgroups (pair wg + r*kv_nwg, round r).  One
+//     XCD's workgroups (consecutive logical ids, xcd_remap) take consecutive
+//     pairs, i.e. the blocks of one or two heads, which stream the same query
+//     tiles and share them in L2; the longer block of a pair goes first.
+//     (Alternating the order between neighbouring workgroups, so that they
+//     stream different tiles, measured the same.)
+//   no mask: every item has the same tiles; items in head-major order are
+//     dealt round-robin (item wg + r*kv_nwg), so that one XCD's workgroups
+//     again hold consecutive key blocks of one or two heads in each round.
+struct KvItem {
+  int bh, kb;
+  int tb;  // first (lowest) query tile of the item; nqt: no query reaches its keys
+};
+
+template <bool CAUSAL>
+__device__ __forceinline__ bool kv_item(const BwdArgs& a, int wg, int m, int nqt, KvItem& it) {
+  const int nkb = a.kv_nkb;
+  if (CAUSAL) {
+    const int npair = (nkb + 1) >> 1;
+    const int q = wg + (m >> 1) * a.kv_nwg;
+    if (q >= a.BH * npair) return false;
+    it.bh = q / npair;
+    const int k = q - it.bh * npair;
+    it.kb = (m & 1) ? nkb - 1 - k : k;
+    // the middle block of an odd count pairs with itself: walked once
+    it.tb = ((m & 1) && nkb - 1 - k == k) ? -1 : min(it.kb * (kKvBlock / 32), nqt);
+  } else {
+    const int i = wg + m * a.kv_nwg;
+    if (i >= a.BH * nkb) return false;
+    it.bh = i / nkb;
+    it.kb = i - it.bh * nkb;
+    it.tb = 0;
+  }
+  return true;
+}
+
+// Position in a workgroup's tile stream: item m - 1 of its list, tile t.
+struct KvCursor {
+  KvItem it;
+  int m, t;
+};
+
+// Moves to the first tile of the next item that has one (items no query
+// reaches are written by the zero pass instead); false at the end of the list.
+template <bool CAUSAL>
+__device__ __forceinline__ bool kv_seek(const BwdArgs& a, int wg, int nqt, KvCursor& c) {
+  while (kv_item<CAUSAL>(a, wg, c.m, nqt, c.it)) {
+    ++c.m;
+    if (c.it.tb >= 0 && c.it.tb < nqt) {
+      c.t = nqt - 1;
+      return true;
+    }
+  }
+  return false;
+}
+template <bool CAUSAL>
+__device__ __forceinline__ bool kv_step(const BwdArgs& a, int wg, int nqt, KvCursor& c) {
+  return --c.t >= c.it.tb || kv_seek<CAUSAL>(a, wg, nqt, c);
+}
+
+// dK = scale * (dK^T)^T and dV of one item's 128 keys, bf16.  Register r of
+// accumulator i is column 32cb + 8(r/4) + 4hf + r%4 of key k0 + 32 kgroup(gw, i)
+// + lane%32; lanes l and l+32 (the same key) trade halves with
+// v_permlane32_swap so that each holds 8 consecutive columns and writes them
+// as one 16-byte store.  Buffer stores with the record size set to the rows
+// before Tk drop the rows past it while every store is still issued: the
+// gradient waves count their vector-memory operations to wait for tile
+// copies, so the number of stores per item must not depend on the data.
+template <int D>
+__device__ __forceinline__ void dkdv_store(const BwdArgs& a, const f32x16 (&dkt)[4], const f32x16 (&dvt)[4],
+                                           const KvItem& it, int gw, int lane) {
+  using C = KvCfg<D>;
+  const int lr = lane % 32, hf = lane / 32;
+  const int k0 = it.kb * C::BK;
+  const int rows = min(C::BK, a.Tk - k0);
+  const size_t base = ((size_t)it.bh * a.Tk + k0) * D;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(a.dk + base, 0, rows * D * 2, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(a.dv + base, 0, rows * D * 2, kBufferWord3);
+  const int cb = gw % C::CB;
+#pragma unroll
+  for (int i = 0; i < C::CB; ++i) {
+    const int row = 32 * C::kgroup(gw, i) + lr;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int off = (row * D + 32 * cb + 16 * j + 8 * hf) * 2;
+      // groups 2j (columns 16j + 4hf + 0..3) and 2j+1 (16j + 8 + 4hf + 0..3)
+      auto half_swap = [&](const f32x16& acc, float f) {
+        const unsigned x0 = pack_bf16x2(acc[8 * j] * f, acc[8 * j + 1] * f);
+        const unsigned x1 = pack_bf16x2(acc[8 * j + 2] * f, acc[8 * j + 3] * f);
+        const unsigned y0 = pack_bf16x2(acc[8 * j + 4] * f, acc[8 * j + 5] * f);
+        const unsigned y1 = pack_bf16x2(acc[8 * j + 6] * f, acc[8 * j + 7] * f);
+        const auto r0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+        const auto r1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+        return u32x4{(unsigned)r0[0], (unsigned)r1[0], (unsigned)r0[1], (unsigned)r1[1]};
+      };
+      __builtin_amdgcn_raw_buffer_store_b128(half_swap(dkt[i], a.scale), rk, off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(half_swap(dvt[i], 1.f), rv, off, 0, 0);
+    }
+  }
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512, D == 64 ? 4 : 1) void bwd_dkdv_kernel(BwdArgs a) {
   using C = KvCfg<D>;
   __shared__ __attribute__((aligned(1024))) __bf16 stages[C::NSTAGE * C::STAGE];
   __shared__ __attribute__((aligned(1024))) __bf16 hands[2 * C::HAND];
@@ -283,72 +422,52 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   const int lr = lane % 32, hf = lane / 32;
-  // A workgroup owns KPW consecutive key blocks of one head (WALK, without
-  // the causal mask; else KPW = 1) and walks the query tiles of each in turn;
-  // with KPW > 1 the query-tile stream runs on across the blocks without
-  // draining.
-  static_assert(!(CAUSAL && WALK), "the key-block walk is for launches without the causal mask");
-  const int KPW = WALK ? a.kv_blocks_per_wg : 1;
-  const int nkb = (a.Tk + C::BK - 1) / C::BK;
-  const int wg_per_head = (nkb + KPW - 1) / KPW;
-  const int item = xcd_remap(blockIdx.x, a.BH * wg_per_head);
-  const int kb0 = (item % wg_per_head) * KPW;  // lowest key block (most causal work) first within a head
-  const int bh = item / wg_per_head;
-  const int nb = min(KPW, nkb - kb0);
+  const int wg = xcd_remap(blockIdx.x, a.kv_nwg);
   const int grp = wave & 3;
-
   const int nqt = (a.Tq + 31) / 32;
-  const int t_begin = CAUSAL ? min(kb0 * C::BK / 32, nqt) : 0;
-  const int n = nqt - t_begin;  // query tiles per key block
-  const int nsteps = nb * n;
-  // Step g covers tile g % n of key block g / n.  Query tiles are walked from
-  // the last one down, so that the key blocks of one head (neighbours on one
-  // XCD) stream the same tiles at about the same time and share them in L2.
-  // (one block: g < n except for the final step, and no division is needed)
-  auto tile = [&](int g) { return nqt - 1 - (WALK ? g % n : g); };
-  auto block = [&](int g) { return WALK ? g / n : 0; };
   auto stage = [&](int g) { return stages + (g % C::NSTAGE) * C::STAGE; };
   auto hand = [&](int g) { return hands + (g & 1) * C::HAND + grp * C::HAND_GRP; };
 
-  // Step g (g = 0..nsteps): tile g has landed and is published by the barrier;
-  // the copy of tile g+AHEAD goes into the stage of tile g-2; score waves work
-  // on tile g, gradient waves on tile g-1.
-  if (wave >= 4)
-    for (int g = 0; g < C::AHEAD && g < nsteps; ++g) dkdv_issue<D>(a, bh, tile(g), stage(g), grp, lane);
-  // a gradient wave's copies of tiles g+1 .. g+AHEAD-1 may still be in flight
-  auto wait_tile = [&](int g) {
-    const int later = min(C::AHEAD - 1, nsteps - 1 - g);
-    if (later >= 3) wait_vm<3 * C::VM>();
-    else if (later == 2) wait_vm<2 * C::VM>();
-    else if (later == 1) wait_vm<C::VM>();
-    else wait_vm<0>();
-  };
-  static_assert(C::AHEAD >= 1 && C::AHEAD <= 4, "wait_tile covers up to 3 later tiles");
+  // Step g (g = 0 .. S, S tiles in the workgroup's stream): tile g has landed
+  // and is published by the barrier; the copy of tile g+AHEAD goes into the
+  // stage of tile g-2; score waves work on tile g, gradient waves on tile
+  // g-1.  Both roles pass S+1 barriers.
+  static_assert(C::AHEAD == 2, "the gradient waves' waits assume copies two tiles ahead");
   if (wave < 4) {
-    bf16x8 kf[8], vf[8];
-    // K and V rows of this wave's 32 keys of key block b, as B operands
-    auto load_keys = [&](int b) {
-      const __bf16* Kh = a.k + (size_t)bh * a.Tk * D;
-      const __bf16* Vh = a.v + (size_t)bh * a.Tk * D;
-      const int kr = min((kb0 + b) * C::BK + 32 * grp + lr, a.Tk - 1);
+    // K and V rows of this wave's 32 keys of an item's key block, as B
+    // operands.  At d = 128 two register sets alternate between consecutive
+    // items: the next item's rows are loaded while the current item runs
+    // (loaded at the item boundary instead, they took about 8 us to arrive
+    // behind the tile copies in flight).  At d = 64 one set, reloaded at the
+    // boundary, keeps the kernel within 128 registers (two workgroups per CU).
+    constexpr bool PREFETCH = D == 128;
+    bf16x8 k0[C::KS], v0[C::KS], k1[C::KS], v1[C::KS];
+    auto load_keys = [&](const KvItem& it, bf16x8(&kf)[C::KS], bf16x8(&vf)[C::KS]) {
+      const __bf16* Kh = a.k + (size_t)it.bh * a.Tk * D;
+      const __bf16* Vh = a.v + (size_t)it.bh * a.Tk * D;
+      const int kr = min(it.kb * C::BK + 32 * grp + lr, a.Tk - 1);
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
         kf[ks] = ld16(Kh + (size_t)kr * D + 16 * ks + 8 * hf);
         vf[ks] = ld16(Vh + (size_t)kr * D + 16 * ks + 8 * hf);
       }
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        settle(kf[ks]);
-        settle(vf[ks]);
-      }
     };
-    load_keys(0);
-    for (int g = 0; g <= nsteps; ++g) {
-      barrier();
-      if (WALK && g < nsteps && g > 0 && g % n == 0) load_keys(g / n);  // next key block
-      if (g < nsteps) {
-        const int t = tile(g);
-        const int kw = (kb0 + block(g)) * C::BK + 32 * grp;
+    KvCursor c;
+    c.m = 0;
+    bool live = kv_seek<CAUSAL>(a, wg, nqt, c);
+    if (live) load_keys(c.it, k0, v0);
+    int g = 0;
+    // The steps of the cursor's item with keys (kf, vf); the next item's keys
+    // go into (kn, vn).  False when the list has no next item.
+    auto run_item = [&](const bf16x8(&kf)[C::KS], const bf16x8(&vf)[C::KS], bf16x8(&kn)[C::KS],
+                        bf16x8(&vn)[C::KS]) __attribute__((always_inline)) {
+      KvCursor nx = c;
+      nx.t = nx.it.tb;
+      const bool more = kv_step<CAUSAL>(a, wg, nqt, nx);
+      if (PREFETCH && more) load_keys(nx.it, kn, vn);
+      const int kw = c.it.kb * C::BK + 32 * grp;
+      for (int t = nqt - 1; t >= c.it.tb; --t, ++g) {
+        barrier();
         // a tile is skipped when the group lies past the keys, or when every
         // query of it precedes every key of the group
         if (kw >= a.Tk || (CAUSAL && 32 * t + 31 < kw)) {
@@ -364,7 +483,20 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
           dkdv_scores<D, false>(a, kf, vf, stage(g), hand(g), t, kw, lane);
         }
       }
+      if (!PREFETCH && more) load_keys(nx.it, kn, vn);
+      c = nx;
+      return more;
+    };
+    while (live) {
+      if (!PREFETCH) {
+        live = run_item(k0, v0, k0, v0);
+        continue;
+      }
+      live = run_item(k0, v0, k1, v1);
+      if (!live) break;
+      live = run_item(k1, v1, k0, v0);
     }
+    barrier();  // step S
   } else {
     f32x16 dkt[4], dvt[4];
 #pragma unroll
@@ -372,51 +504,59 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
       dkt[cb] = f32x16{};
       dvt[cb] = f32x16{};
     }
-    // dK = scale * (dK^T)^T, dV of key block b: register r of accumulator i is
-    // column 32cb + 8(r/4) + 4hf + r%4 of key k0 + 32 kgroup(grp, i) + lane%32
-    auto store_block = [&](int b) {
-      const int k0 = (kb0 + b) * C::BK;
-      const int cb = grp % C::CB;
-#pragma unroll
-      for (int i = 0; i < C::CB; ++i) {
-        const int kk = k0 + 32 * C::kgroup(grp, i) + lr;
-        if (kk >= a.Tk) continue;
-        __bf16* dkr = a.dk + ((size_t)bh * a.Tk + kk) * D;
-        __bf16* dvr = a.dv + ((size_t)bh * a.Tk + kk) * D;
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int c = 32 * cb + 8 * g4 + 4 * hf;
-          const u32x2 wk = {pack_bf16x2(dkt[i][4 * g4] * a.scale, dkt[i][4 * g4 + 1] * a.scale),
-                            pack_bf16x2(dkt[i][4 * g4 + 2] * a.scale, dkt[i][4 * g4 + 3] * a.scale)};
-          const u32x2 wv = {pack_bf16x2(dvt[i][4 * g4], dvt[i][4 * g4 + 1]),
-                            pack_bf16x2(dvt[i][4 * g4 + 2], dvt[i][4 * g4 + 3])};
-          *reinterpret_cast<u32x2*>(dkr + c) = wk;
-          *reinterpret_cast<u32x2*>(dvr + c) = wv;
-        }
+    // items no query reaches (causal, keys past Tq) get zero gradients
+    // before the stream starts
+    if (CAUSAL && a.kv_zero_items) {
+      KvItem it;
+      for (int m = 0; kv_item<CAUSAL>(a, wg, m, nqt, it); ++m)
+        if (it.tb == nqt) dkdv_store<D>(a, dkt, dvt, it, grp, lane);
+    }
+    KvCursor ci, cg;  // the next tile to copy, the tile the gradient step takes
+    ci.m = 0;
+    bool li = kv_seek<CAUSAL>(a, wg, nqt, ci);
+    cg = ci;
+    bool lg = li;
+    int issued = 0;
+    for (int j = 0; j < C::AHEAD && li; ++j) {
+      dkdv_issue<D>(a, ci.it.bh, ci.t, stage(issued++), grp, lane);
+      li = kv_step<CAUSAL>(a, wg, nqt, ci);
+    }
+    // Vector-memory operations after tile g's copies, in issue order: the
+    // stores of step g-2, the copies of tile g+1, the stores of step g-1
+    // (operations complete in issue order, so waiting until at most that many
+    // are outstanding waits for tile g).
+    constexpr int NST = 4 * C::CB;  // stores per item and wave
+    bool st1 = false, st2 = false;  // stores issued in steps g-1, g-2
+    for (int g = 0;; ++g) {
+      if (g < issued) {
+        const int k = (st1 ? 1 : 0) + (st2 ? 1 : 0);
+        const bool later = g + 1 < issued;
+        if (k == 0) later ? wait_vm<C::VM>() : wait_vm<0>();
+        else if (k == 1) later ? wait_vm<NST + C::VM>() : wait_vm<NST>();
+        else later ? wait_vm<2 * NST + C::VM>() : wait_vm<2 * NST>();
       }
-    };
-    for (int g = 0; g <= nsteps; ++g) {
-      wait_tile(g);
       barrier();
-      if (g + C::AHEAD < nsteps) dkdv_issue<D>(a, bh, tile(g + C::AHEAD), stage(g + C::AHEAD), grp, lane);
-      // every tile in range has an active key group (the first one); score
-      // waves of inactive groups hand over zeros
+      if (li) {
+        dkdv_issue<D>(a, ci.it.bh, ci.t, stage(issued++), grp, lane);
+        li = kv_step<CAUSAL>(a, wg, nqt, ci);
+      }
+      st2 = st1;
+      st1 = false;
       if (g >= 1) {
         dkdv_grads<D>(dkt, dvt, stage(g - 1), hands + ((g - 1) & 1) * C::HAND, grp, lane);
-        if (WALK && g % n == 0 && g < nsteps) {
-          // tile g-1 closed key block g/n - 1: write it, start the next
-          store_block(g / n - 1);
+        if (cg.t == cg.it.tb) {  // tile g-1 closed its item
+          dkdv_store<D>(a, dkt, dvt, cg.it, grp, lane);
 #pragma unroll
           for (int cb = 0; cb < C::CB; ++cb) {
             dkt[cb] = f32x16{};
             dvt[cb] = f32x16{};
           }
+          st1 = true;
         }
+        lg = kv_step<CAUSAL>(a, wg, nqt, cg);
       }
+      if (!lg) break;
     }
-    // the last (or only) block; zeros when no query reaches it (causal keys
-    // past every query)
-    store_block(nb - 1);
   }
 }
 
@@ -439,7 +579,7 @@ struct DqCfg {
 struct DqWave {
   bf16x8 qf[8], df[8];  // Q, dO rows of this lane's query as B operands
   f32x16 dqt[4];
-  float lse2, dsum;
+  float lse2, ndsum;  // LSE * log2(e), -D of this lane's query
 };
 
 template <int D>
@@ -471,7 +611,7 @@ __device__ __forceinline__ void dq_softmax(const BwdArgs& a, const DqWave& w, co
       const int kk = key0 + 8 * (r / 4) + 4 * hf + (r % 4);
       p = ((CAUSAL && kk > my_q) || kk >= a.Tk) ? 0.f : p;
     }
-    db[r / 8][r % 8] = to_bf16(p * (dpt[r] - w.dsum));
+    db[r / 8][r % 8] = to_bf16(p * (dpt[r] + w.ndsum));
   }
 }
 
@@ -580,11 +720,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int cb = 0; cb < C::CB; ++cb) w.dqt[cb] = f32x16{};
     w.lse2 = INFINITY;
-    w.dsum = 0.f;
+    w.ndsum = 0.f;
     if (my_q < a.Tq) {
-      const float* blk = a.stats + ((size_t)bh * a.nqb32 + my_q / 32) * 64;
+      const float* blk = a.stats + ((size_t)bh * a.nqb32 + my_q / 32) * kStatsPerBlock;
       w.lse2 = blk[my_q % 32];
-      w.dsum = blk[32 + my_q % 32];
+      w.ndsum = blk[64 + my_q % 32];
     }
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
@@ -592,7 +732,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a) {
       settle(w.df[ks]);
     }
     settle(w.lse2);
-    settle(w.dsum);
+    settle(w.ndsum);
   }
 
   const int nkt_all = (a.Tk + 63) / 64;
@@ -698,25 +838,28 @@ BwdLayout bwd_layout(int BH, int Tq, int Tk, int d, int dq_splits) {
   const DqSplit sp = dq_split(Tk, dq_splits);
   BwdLayout L;
   L.stats = 0;
-  L.dq_part = up(L.stats + (size_t)BH * nqb32 * 64 * sizeof(float));
+  L.dq_part = up(L.stats + (size_t)BH * nqb32 * kStatsPerBlock * sizeof(float));
   L.total = L.dq_part + (sp.splits > 1 ? up((size_t)sp.splits * BH * Tq * d * sizeof(float)) : 0);
   return L;
 }
 
-// Key blocks per dK/dV workgroup without the causal mask: with very few query
-// tiles (at most 8, Tq <= 256) a workgroup's fill and drain (K/V rows loaded,
-// the query-tile stream started, dK/dV written) weigh on its few steps, so one
-// workgroup walks several consecutive key blocks of a head (about 128
-// query-tile steps), as long as the launch keeps at least two workgroups per
-// CU.  (Measured: Tq=256 Tk=65536 backward 2.84 vs 2.98 ms; with 64 query
-// tiles a 2-block walk was 9% slower, so longer query ranges keep one block.)
-int dkdv_blocks_per_wg(int BH, int Tq, int nkb) {
-  const int nqt = (Tq + 31) / 32;
-  if (nqt > 8) return 1;
-  int kpw = std::max(1, 128 / nqt);
-  kpw = std::min(kpw, nkb);
-  while (kpw > 1 && (long long)BH * ((nkb + kpw - 1) / kpw) < 512) kpw /= 2;
-  return kpw;
+// Workgroups of kernel K (512 threads, static LDS only) that the current
+// device holds at once: CUs x workgroups per CU; 0 when the device cannot be
+// queried.  Cached per device.
+template <auto K>
+int resident_workgroups() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0, per = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, K, 512, 0) != hipSuccess) return 0;
+  v = cus * std::max(per, 1);
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
 }
 
 template <int D>
@@ -729,22 +872,26 @@ hipError_t bwd_launch_d(BwdArgs& args, const __bf16* o, const float* lse, const 
     const size_t rows = (size_t)args.BH * args.nqb32 * 32;
     const unsigned blocks = (unsigned)std::min<size_t>((rows + 15) / 16, (size_t)1 << 20);
     hipLaunchKernelGGL(bwd_stats_kernel<D>, dim3(blocks), dim3(256), 0, stream, o, args.dout, lse, dlse,
-                       reinterpret_cast<float*>(ws + L.stats), args.BH, args.Tq, args.nqb32);
+                       reinterpret_cast<float*>(ws + L.stats), args.BH, args.Tq, args.nqb32, args.scale);
   }
   prof_end(2, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
   const int nkb = (args.Tk + KvCfg<D>::BK - 1) / KvCfg<D>::BK;
-  args.kv_blocks_per_wg = causal ? 1 : dkdv_blocks_per_wg(args.BH, args.Tq, nkb);
-  const int wg_per_head = (nkb + args.kv_blocks_per_wg - 1) / args.kv_blocks_per_wg;
+  const int nqt = (args.Tq + 31) / 32;
+  const long long items = causal ? (long long)args.BH * ((nkb + 1) / 2) : (long long)args.BH * nkb;
+  const int resident = causal ? resident_workgroups<bwd_dkdv_kernel<D, true>>()
+                              : resident_workgroups<bwd_dkdv_kernel<D, false>>();
+  if (resident <= 0) return hipErrorInvalidDevice;
+  args.kv_nkb = nkb;
+  args.kv_nwg = (int)std::min<long long>(items, resident);
+  args.kv_zero_items = causal && (nkb - 1) * (KvCfg<D>::BK / 32) >= nqt;
   prof_begin(3, stream);
   if (causal)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, false>), dim3(args.BH * nkb), dim3(512), 0, stream, args);
-  else if (args.kv_blocks_per_wg > 1)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, true>), dim3(args.BH * wg_per_head), dim3(512), 0, stream, args);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(args.kv_nwg), dim3(512), 0, stream, args);
   else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, false>), dim3(args.BH * nkb), dim3(512), 0, stream, args);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(args.kv_nwg), dim3(512), 0, stream, args);
   prof_end(3, stream);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
