@@ -6,7 +6,29 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 
+#include <algorithm>
+#include <atomic>
+
 namespace attn {
+
+// Workgroups of kernel K (`threads` per workgroup, static LDS only) that the
+// current device holds at once: CUs x workgroups per CU, the grid of a
+// persistent launch; 0 when the device cannot be queried.  Cached per device.
+template <auto K>
+int resident_workgroups(int threads) {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0, per = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, K, threads, 0) != hipSuccess) return 0;
+  v = cus * std::max(per, 1);
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
 
 // Event profiler hooks (defined in api.cpp).  When profiling is off these are
 // a single relaxed load each.

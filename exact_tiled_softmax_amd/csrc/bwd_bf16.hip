@@ -40,7 +40,6 @@
 // tiles are copied global -> LDS by the direct-to-LDS vector load, several
 // tiles ahead of the compute.
 #include <algorithm>
-#include <atomic>
 #include <mutex>
 
 #include "attn.h"
@@ -843,25 +842,6 @@ BwdLayout bwd_layout(int BH, int Tq, int Tk, int d, int dq_splits) {
   return L;
 }
 
-// Workgroups of kernel K (512 threads, static LDS only) that the current
-// device holds at once: CUs x workgroups per CU; 0 when the device cannot be
-// queried.  Cached per device.
-template <auto K>
-int resident_workgroups() {
-  constexpr int kMaxDev = 64;
-  static std::atomic<int> cache[kMaxDev];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
-  int v = cache[dev].load(std::memory_order_relaxed);
-  if (v > 0) return v;
-  int cus = 0, per = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, K, 512, 0) != hipSuccess) return 0;
-  v = cus * std::max(per, 1);
-  cache[dev].store(v, std::memory_order_relaxed);
-  return v;
-}
-
 template <int D>
 hipError_t bwd_launch_d(BwdArgs& args, const __bf16* o, const float* lse, const float* dlse, bool causal, char* ws,
                         const BwdLayout& L, hipStream_t stream) {
@@ -881,8 +861,8 @@ hipError_t bwd_launch_d(BwdArgs& args, const __bf16* o, const float* lse, const 
   const int nkb = (args.Tk + KvCfg<D>::BK - 1) / KvCfg<D>::BK;
   const int nqt = (args.Tq + 31) / 32;
   const long long items = causal ? (long long)args.BH * ((nkb + 1) / 2) : (long long)args.BH * nkb;
-  const int resident = causal ? resident_workgroups<bwd_dkdv_kernel<D, true>>()
-                              : resident_workgroups<bwd_dkdv_kernel<D, false>>();
+  const int resident = causal ? resident_workgroups<bwd_dkdv_kernel<D, true>>(512)
+                              : resident_workgroups<bwd_dkdv_kernel<D, false>>(512);
   if (resident <= 0) return hipErrorInvalidDevice;
   args.kv_nkb = nkb;
   args.kv_nwg = (int)std::min<long long>(items, resident);

@@ -1,7 +1,8 @@
 // Forward pass of exact tiled-softmax attention, bf16 in / bf16 out, for
 // gfx950 (MI355X).
 //
-// One workgroup of 8 waves owns a tile of 256 query rows of one (batch, head)
+// A workgroup of 8 waves owns a tile of 256 query rows of one (batch, head)
+// at a time (at d = 128 a persistent workgroup runs a list of such tiles)
 // (the "inner-outer loop exchange" of "The Hidden Recurrence in Softmax
 // Attention", section "Chunk-wise Mode with Online Softmax Re-scale": query
 // tiles outside, key tiles inside).  Each wave owns 32 rows and keeps, per
@@ -40,6 +41,7 @@
 // With key splits, each workgroup covers one contiguous key range and stores
 // its unnormalised state (m, l, a) in fp32; a second kernel merges the states
 // of a row with the same rescale rule and writes O and LSE.
+#include <algorithm>
 #include <type_traits>
 
 #include "attn_common.hpp"
@@ -71,7 +73,13 @@ struct FwdCfg {
   static constexpr int STAGE = 2 * TILE;
   static constexpr int NSTAGE = 4;
   static constexpr int AHEAD = NSTAGE - 1;               // tiles in flight ahead of the compute
-  static constexpr int WG_PER_CU = 1;
+  // waves per SIMD the register budget is set for: two workgroups per CU at
+  // d = 64 (64 KB of LDS each), one at d = 128
+  static constexpr int WAVES_PER_SIMD = D == 64 ? 4 : 2;
+  // d = 128: persistent workgroups, each running a list of items; d = 64:
+  // one workgroup per item (two share a CU, hiding each other's fill and
+  // drain, and the item loop would not fit the 128-register budget)
+  static constexpr bool PERSIST = D == 128;
   static_assert(PER_WAVE >= 1 && 2 * PER_TENSOR == PER_WAVE * WAVES, "tile copy split");
   static_assert(PER_TENSOR % PER_WAVE == 0, "the copies of one wave belong to one tensor");
 };
@@ -88,7 +96,8 @@ struct FwdArgs {
   int BH, Tq, Tk, Tk_pad;
   int diag;          // causal: key j is blocked for query i when j > i + diag
   int num_qtiles, num_splits, keys_per_split;
-  int head_group;    // heads whose query tiles are dispatched interleaved (work_item)
+  int n_items;       // BH * num_qtiles * num_splits
+  int nwg;           // workgroups of the persistent launch
   float scale_log2;  // scale * log2(e)
 };
 
@@ -257,24 +266,55 @@ __device__ __forceinline__ void fwd_tile(const char* stg, const FwdLdsOffsets<D>
       }
 }
 
+// Work list of the forward launch.  At d = 128 the launch is persistent: a.nwg
+// workgroups (as many as the chip holds at once) each run a fixed list of
+// items (head, key split, query tile) one after the other, so that no
+// workgroup waits on the dispatcher between items (with one workgroup per CU
+// a CU idled about 6 us, median, between two workgroups), and the first tile
+// copies of the next item are issued before the current item's outputs are
+// written.  Items are dealt round-robin (item wg + r*nwg in head-major order,
+// query tile fastest): one XCD's workgroups (consecutive logical ids,
+// xcd_remap) hold the query tiles of one or two heads in each round and share
+// their K/V tiles in L2.  Odd rounds take a head's query tiles in reverse
+// order, so that a workgroup's causal work (query tile j, then nq-1-j) evens
+// out over two rounds.
+struct FwdItem {
+  int bh, qt, split;
+  int kbeg, kend, ntiles;  // key range and its 64-key tiles
+};
+
 template <int D, bool CAUSAL, bool SPLIT>
-__global__ __launch_bounds__(FwdCfg<D>::THREADS, FwdCfg<D>::WG_PER_CU) void fwd_bf16_kernel(FwdArgs a) {
+__device__ __forceinline__ bool fwd_item(const FwdArgs& a, int wg, int m, FwdItem& it) {
+  using C = FwdCfg<D>;
+  const int nq = a.num_qtiles;
+  const int i = wg + m * a.nwg;
+  if (i >= a.n_items) return false;
+  const int j = i % nq, rest = i / nq;
+  it.split = SPLIT ? rest % a.num_splits : 0;
+  it.bh = SPLIT ? rest / a.num_splits : rest;
+  it.qt = (m & 1) ? nq - 1 - j : j;
+  int kbeg = 0, kend = a.Tk;
+  if (SPLIT) {
+    kbeg = it.split * a.keys_per_split;
+    kend = min(a.Tk, kbeg + a.keys_per_split);
+  }
+  if (CAUSAL) kend = max(kbeg, min(kend, it.qt * C::BM + C::BM + a.diag));
+  it.kbeg = kbeg;
+  it.kend = kend;
+  it.ntiles = kend > kbeg ? (kend - kbeg + C::BN - 1) / C::BN : 0;
+  return true;
+}
+
+template <int D, bool CAUSAL, bool SPLIT>
+__global__ __launch_bounds__(FwdCfg<D>::THREADS, FwdCfg<D>::WAVES_PER_SIMD) void fwd_bf16_kernel(FwdArgs a) {
   using C = FwdCfg<D>;
   __shared__ __attribute__((aligned(1024))) __bf16 stages[C::NSTAGE * C::STAGE];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   const int lr = lane % 32, hf = lane / 32;
-  const int n_items = a.BH * a.num_qtiles * a.num_splits;
-  // heavier (later) causal query tiles first
-  const WorkItem wi = work_item(xcd_remap(blockIdx.x, n_items), a.BH, a.num_qtiles, a.num_splits, a.head_group);
-  const int split = wi.split;
-  const int qt = a.num_qtiles - 1 - wi.blk;
-  const int bh = wi.bh;
+  const int wg = xcd_remap(blockIdx.x, a.nwg);
 
-  const int q0 = qt * C::BM;
-  const int row = q0 + wave * 32 + lr;  // this lane's query row
-  const __bf16* Qh = a.q + (size_t)bh * a.Tq * D;
   // Tile copies: a tile that lies inside [0, Tk) is copied from a
   // wave-uniform base with per-lane byte offsets computed here once (the
   // layout of fwd_issue); a tile that runs past Tk clamps its rows per lane.
@@ -285,7 +325,7 @@ __global__ __launch_bounds__(FwdCfg<D>::THREADS, FwdCfg<D>::WG_PER_CU) void fwd_
     const int rr = p / C::CPR, cc = (p % C::CPR) ^ swz<C::CPR>(rr);
     voff[n] = (uint32_t)((rr * D + 8 * cc) * (int)sizeof(__bf16));
   }
-  auto issue = [&](int key0, __bf16* stg) {
+  auto issue = [&](int bh, int key0, __bf16* stg) {
     if (key0 + C::BN <= a.Tk) {
       const int tensor = (wave * C::PER_WAVE) / C::PER_TENSOR;  // the same for all copies of a wave
       const __bf16* base = (tensor == 0 ? a.k : a.v) + ((size_t)bh * a.Tk + key0) * D;
@@ -298,100 +338,114 @@ __global__ __launch_bounds__(FwdCfg<D>::THREADS, FwdCfg<D>::WG_PER_CU) void fwd_
       fwd_issue<D>(a, bh, key0, stg, wave, lane);
     }
   };
-
-  int kbeg = 0, kend = a.Tk;
-  if (SPLIT) {
-    kbeg = split * a.keys_per_split;
-    kend = min(a.Tk, kbeg + a.keys_per_split);
-  }
-  if (CAUSAL) kend = max(kbeg, min(kend, q0 + C::BM + a.diag));
-  const int ntiles = kend > kbeg ? (kend - kbeg + C::BN - 1) / C::BN : 0;
-  // end of the keys this wave's rows may see (causal): whole tiles past it are
-  // skipped
-  const int wave_kend = CAUSAL ? min(kend, q0 + wave * 32 + 32 + a.diag) : kend;
-  const int wave_row0 = q0 + wave * 32;
-
-  // Q fragments (B operand of S^T = K Q^T): lane holds Q[row][16*ks + 8*hf + 0..7]
-  bf16x8 qf[8];
-  {
-    const int qr = min(row, a.Tq - 1);
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) qf[ks] = ld16(Qh + (size_t)qr * D + 16 * ks + 8 * hf);
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) settle(qf[ks]);
-  }
-
-  f32x16 acc[4];
-#pragma unroll
-  for (int cb = 0; cb < C::CB; ++cb) acc[cb] = f32x16{};
-  float m_ref = -INFINITY;  // reference max of scaled scores, log2 units
-  float l_run = 0.f;        // this lane's share of the running sum
+  auto stage = [&](int t) { return stages + (t % C::NSTAGE) * C::STAGE; };
+  auto prologue = [&](const FwdItem& it) {
+    for (int t = 0; t < C::AHEAD && t < it.ntiles; ++t) issue(it.bh, it.kbeg + t * C::BN, stage(t));
+  };
+  const FwdLdsOffsets<D> lo = fwd_lds_offsets<D>(lane);
   const float c = a.scale_log2;
 
-  const FwdLdsOffsets<D> lo = fwd_lds_offsets<D>(lane);
-  auto stage = [&](int t) { return stages + (t % C::NSTAGE) * C::STAGE; };
-  for (int t = 0; t < C::AHEAD && t < ntiles; ++t) issue(kbeg + t * C::BN, stage(t));
-  static_assert(C::AHEAD >= 1 && C::AHEAD <= 3, "the waits below cover up to 2 later tiles");
-  static_assert(C::NSTAGE == 4, "the tile loop is unrolled over 4 stages");
-  // tile t in stage S = t % NSTAGE, S a compile-time constant
-  auto step = [&](int t, auto stage_c) {
-    constexpr int S = decltype(stage_c)::value;
-    // this wave's copies of tiles t+1 .. t+AHEAD-1 may still be in flight
-    const int later = min(C::AHEAD - 1, ntiles - 1 - t);
-    if (C::AHEAD >= 3 && later >= 2) wait_vm<2 * C::VM>();
-    else if (C::AHEAD >= 2 && later == 1) wait_vm<C::VM>();
-    else wait_vm<0>();
-    barrier();
-    if (t + C::AHEAD < ntiles) issue(kbeg + (t + C::AHEAD) * C::BN, stages + ((S + C::AHEAD) % C::NSTAGE) * C::STAGE);
-    const int key0 = kbeg + t * C::BN;
-    if (key0 < wave_kend) {
-      const bool need_mask = (key0 + C::BN > kend) || (CAUSAL && key0 + C::BN - 1 > wave_row0 + a.diag);
-      fwd_tile<D>(reinterpret_cast<const char*>(stages + S * C::STAGE), lo, qf, acc, m_ref, l_run, c, lane,
-                  need_mask, key0, kend, row + a.diag, CAUSAL);
-    }
-  };
-  for (int t = 0; t < ntiles; t += C::NSTAGE) {
-    step(t, std::integral_constant<int, 0>{});
-    if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>{});
-    if (t + 2 < ntiles) step(t + 2, std::integral_constant<int, 2>{});
-    if (t + 3 < ntiles) step(t + 3, std::integral_constant<int, 3>{});
-  }
+  FwdItem it;
+  bool have = fwd_item<D, CAUSAL, SPLIT>(a, wg, 0, it);
+  if (have) prologue(it);
+  for (int m = 0; have; ++m) {
+    const int q0 = it.qt * C::BM;
+    const int row = q0 + wave * 32 + lr;  // this lane's query row
+    const int ntiles = it.ntiles, kbeg = it.kbeg, kend = it.kend;
+    // end of the keys this wave's rows may see (causal): whole tiles past it are
+    // skipped
+    const int wave_kend = CAUSAL ? min(kend, q0 + wave * 32 + 32 + a.diag) : kend;
+    const int wave_row0 = q0 + wave * 32;
 
-  // ---- epilogue ------------------------------------------------------------------
-  const float l_tot = pair_sum(l_run);
-  if (SPLIT) {
-    if (row < a.Tq) {
-      const size_t prow = ((size_t)split * a.BH + bh) * a.Tq + row;
-      float* pa = a.part_acc + prow * D;
+    // Q fragments (B operand of S^T = K Q^T): lane holds Q[row][16*ks + 8*hf + 0..7]
+    bf16x8 qf[8];
+    {
+      const __bf16* Qh = a.q + (size_t)it.bh * a.Tq * D;
+      const int qr = min(row, a.Tq - 1);
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) qf[ks] = ld16(Qh + (size_t)qr * D + 16 * ks + 8 * hf);
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) settle(qf[ks]);
+    }
+
+    f32x16 acc[4];
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb) acc[cb] = f32x16{};
+    float m_ref = -INFINITY;  // reference max of scaled scores, log2 units
+    float l_run = 0.f;        // this lane's share of the running sum
+
+    static_assert(C::AHEAD >= 1 && C::AHEAD <= 3, "the waits below cover up to 2 later tiles");
+    static_assert(C::NSTAGE == 4, "the tile loop is unrolled over 4 stages");
+    // tile t in stage S = t % NSTAGE, S a compile-time constant
+    auto step = [&](int t, auto stage_c) {
+      constexpr int S = decltype(stage_c)::value;
+      // this wave's copies of tiles t+1 .. t+AHEAD-1 may still be in flight
+      const int later = min(C::AHEAD - 1, ntiles - 1 - t);
+      if (C::AHEAD >= 3 && later >= 2) wait_vm<2 * C::VM>();
+      else if (C::AHEAD >= 2 && later == 1) wait_vm<C::VM>();
+      else wait_vm<0>();
+      barrier();
+      if (t + C::AHEAD < ntiles)
+        issue(it.bh, kbeg + (t + C::AHEAD) * C::BN, stages + ((S + C::AHEAD) % C::NSTAGE) * C::STAGE);
+      const int key0 = kbeg + t * C::BN;
+      if (key0 < wave_kend) {
+        const bool need_mask = (key0 + C::BN > kend) || (CAUSAL && key0 + C::BN - 1 > wave_row0 + a.diag);
+        fwd_tile<D>(reinterpret_cast<const char*>(stages + S * C::STAGE), lo, qf, acc, m_ref, l_run, c, lane,
+                    need_mask, key0, kend, row + a.diag, CAUSAL);
+      }
+    };
+    for (int t = 0; t < ntiles; t += C::NSTAGE) {
+      step(t, std::integral_constant<int, 0>{});
+      if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>{});
+      if (t + 2 < ntiles) step(t + 2, std::integral_constant<int, 2>{});
+      if (t + 3 < ntiles) step(t + 3, std::integral_constant<int, 3>{});
+    }
+
+    // the next item's first tile copies go out before this item's outputs:
+    // every wave is done with the stages once all have passed this barrier
+    const FwdItem cur = it;
+    if constexpr (C::PERSIST) {
+      have = fwd_item<D, CAUSAL, SPLIT>(a, wg, m + 1, it);
+      barrier();
+      if (have) prologue(it);
+    } else {
+      have = false;
+    }
+
+    // ---- epilogue ------------------------------------------------------------------
+    const float l_tot = pair_sum(l_run);
+    if (SPLIT) {
+      if (row < a.Tq) {
+        const size_t prow = ((size_t)cur.split * a.BH + cur.bh) * a.Tq + row;
+        float* pa = a.part_acc + prow * D;
+#pragma unroll
+        for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int cc = 32 * cb + 8 * g + 4 * hf;
+            *reinterpret_cast<f32x4*>(pa + cc) =
+                f32x4{acc[cb][4 * g], acc[cb][4 * g + 1], acc[cb][4 * g + 2], acc[cb][4 * g + 3]};
+          }
+        if (hf == 0) {
+          a.part_m[prow] = m_ref * kLn2;  // -inf stays -inf
+          a.part_l[prow] = l_tot;
+        }
+      }
+    } else if (row < a.Tq) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      __bf16* orow = a.o + ((size_t)cur.bh * a.Tq + row) * D;
 #pragma unroll
       for (int cb = 0; cb < C::CB; ++cb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int cc = 32 * cb + 8 * g + 4 * hf;
-          *reinterpret_cast<f32x4*>(pa + cc) =
-              f32x4{acc[cb][4 * g], acc[cb][4 * g + 1], acc[cb][4 * g + 2], acc[cb][4 * g + 3]};
+          u32x2 w = {pack_bf16x2(acc[cb][4 * g] * inv, acc[cb][4 * g + 1] * inv),
+                     pack_bf16x2(acc[cb][4 * g + 2] * inv, acc[cb][4 * g + 3] * inv)};
+          *reinterpret_cast<u32x2*>(orow + cc) = w;
         }
       if (hf == 0) {
-        a.part_m[prow] = m_ref * kLn2;  // -inf stays -inf
-        a.part_l[prow] = l_tot;
+        a.lse[(size_t)cur.bh * a.Tq + row] = l_tot > 0.f ? (m_ref + fast_log2(l_tot)) * kLn2 : -INFINITY;
       }
-    }
-    return;
-  }
-  if (row < a.Tq) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    __bf16* orow = a.o + ((size_t)bh * a.Tq + row) * D;
-#pragma unroll
-    for (int cb = 0; cb < C::CB; ++cb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int cc = 32 * cb + 8 * g + 4 * hf;
-        u32x2 w = {pack_bf16x2(acc[cb][4 * g] * inv, acc[cb][4 * g + 1] * inv),
-                   pack_bf16x2(acc[cb][4 * g + 2] * inv, acc[cb][4 * g + 3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + cc) = w;
-      }
-    if (hf == 0) {
-      a.lse[(size_t)bh * a.Tq + row] = l_tot > 0.f ? (m_ref + fast_log2(l_tot)) * kLn2 : -INFINITY;
     }
   }
 }
@@ -434,10 +488,12 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(const float* __restric
 }
 
 template <int D, bool CAUSAL, bool SPLIT>
-hipError_t launch_fwd(const FwdArgs& args, hipStream_t stream) {
-  const int n = args.BH * args.num_qtiles * args.num_splits;
+hipError_t launch_fwd(FwdArgs args, hipStream_t stream) {
+  const int resident = resident_workgroups<fwd_bf16_kernel<D, CAUSAL, SPLIT>>(FwdCfg<D>::THREADS);
+  if (resident <= 0) return hipErrorInvalidDevice;
+  args.nwg = FwdCfg<D>::PERSIST ? std::min(args.n_items, resident) : args.n_items;
   prof_begin(0, stream);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, SPLIT>), dim3(n), dim3(FwdCfg<D>::THREADS), 0, stream, args);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, SPLIT>), dim3(args.nwg), dim3(FwdCfg<D>::THREADS), 0, stream, args);
   prof_end(0, stream);
   return hipGetLastError();
 }
@@ -518,7 +574,7 @@ FwdArgs fwd_args(const void* q, const void* k, const void* v, void* o, float* ls
   args.num_splits = num_splits;
   const int kblocks = (Tk + kBN - 1) / kBN;
   args.keys_per_split = ((kblocks + num_splits - 1) / num_splits) * kBN;
-  args.head_group = head_group(BH, args.num_qtiles * num_splits);
+  args.n_items = BH * args.num_qtiles * num_splits;
   args.scale_log2 = scale * kLog2e;
   return args;
 }
