@@ -78,18 +78,18 @@ def work(w):
 
 def kernel_bytes(w):
     """Algorithmic HBM bytes per launch of each kernel: what it must read
-    (every input once) and write (every output once).  The backward's row
-    statistics are 12 bytes per query row (LSE*log2(e), -LSE/scale and -D,
-    fp32), of which the dK/dV and dQ kernels each read 8."""
+    (every input once) and write (every output once).  The dQ kernel reads
+    O and LSE besides its own inputs and writes the row statistics the dK/dV
+    kernel reads (8 bytes per query row: -LSE/scale and -D, fp32)."""
     e = 2  # bf16 bytes
     bh = w.B * w.H
     qo = e * (w.Tq * w.d + w.Tq * w.dv)  # Q and dO (or Q and O)
     kv = e * (w.Tk * w.d + w.Tk * w.dv)  # K and V
     return {
         "fwd": bh * (qo + kv + 4 * w.Tq),
-        "bwd_prep": bh * (2 * e * w.Tq * w.dv + 4 * w.Tq + 12 * w.Tq),
+        "bwd_prep": 0,
         "bwd_dkdv": bh * (qo + kv + 8 * w.Tq + kv),
-        "bwd_dq": bh * (qo + kv + 8 * w.Tq + e * w.Tq * w.d),
+        "bwd_dq": bh * (qo + kv + e * w.Tq * w.dv + 4 * w.Tq + 8 * w.Tq + e * w.Tq * w.d),
     }
 
 

@@ -14,27 +14,27 @@
 // keys), so they come from two kernels that each keep their own accumulator
 // in registers and write it once; no workgroup adds into another's output.
 // Kernels, in launch order:
-//   bwd_stats      per query row: LSE * log2(e) and -LSE / scale (+inf and
-//                  -inf for a row that is outside Tq or has no allowed key,
-//                  so its P is 0) and -D, D = sum_c dO_c O_c, blocked 32 rows
-//                  at a time.  With an
-//                  upstream gradient dLSE on the log-sum-exp, dS gains
-//                  dLSE_i P_ij (the row sum l is a smooth function of the
-//                  inputs that gradients flow through: "The Hidden Recurrence
-//                  in Softmax Attention", sections "Flash Attention Backward
-//                  Pass" and "Gradient at the Output"), i.e. D becomes D - dLSE.
+//   bwd_dq         one workgroup (8 waves) per 256 queries; each wave keeps
+//                  its 32 queries' Q and dO rows as MFMA operands and dQ^T in
+//                  registers and walks 64-key tiles streamed into LDS:
+//                    S^T = K Q^T, dP^T = V dO^T, P^T = exp2(S^T*scale*log2e
+//                    - LSE*log2e), dS^T = P^T o (dP^T - D),
+//                    dQ^T += K^T dS^T (K^T fragments by transposing reads of
+//                    the row-major K tile already in LDS)
+//                  It first forms each row's statistics from the forward's
+//                  LSE and O: D = sum_c dO_c O_c (with an upstream gradient
+//                  dLSE on the log-sum-exp, dS gains dLSE_i P_ij: the row sum
+//                  l is a smooth function of the inputs that gradients flow
+//                  through, "The Hidden Recurrence in Softmax Attention",
+//                  sections "Flash Attention Backward Pass" and "Gradient at
+//                  the Output", i.e. D becomes D - dLSE), and writes -LSE/scale
+//                  and -D for the dK/dV kernel.
 //   bwd_dkdv       persistent: each workgroup (8 waves) runs a fixed list of
 //                  128-key blocks back to back, walking 32-query tiles
 //                  streamed into LDS (see the kernel's comment):
 //                    S' = Q K^T - LSE/scale, dP' = dO V^T - D (both from the
 //                    MFMA accumulators' start values), P = exp2(S'*scale*log2e),
 //                    dS = P o dP', dV^T += dO^T P, dK^T += Q^T dS
-//   bwd_dq         one workgroup (8 waves) per 256 queries; each wave keeps
-//                  its 32 queries' Q and dO rows as MFMA operands and dQ^T in
-//                  registers and walks 64-key tiles streamed into LDS:
-//                    S^T = K Q^T, dP^T = V dO^T, dS^T as above,
-//                    dQ^T += K^T dS^T (K^T fragments by transposing reads of
-//                    the row-major K tile already in LDS)
 // LDS tiles have their 16-byte chunks XOR-swizzled per row so that both
 // 16-byte row reads and transposing reads are free of bank conflicts, and
 // tiles are copied global -> LDS by the direct-to-LDS vector load, several
@@ -52,17 +52,20 @@ namespace attn {
 
 namespace {
 
-// Row statistics of one 32-row block: LSE * log2(e) (the dQ kernel's
-// exponent offset), -LSE / scale and -D (the dK/dV kernel's accumulator
-// start values, so that its MFMAs produce S - LSE/scale and dP - D).
-constexpr int kStatsPerBlock = 96;
+// Row statistics of one 32-row block, written by the dQ kernel and read by the
+// dK/dV kernel: -LSE / scale and -D, the start values of the dK/dV kernel's
+// MFMA accumulators (its MFMAs then produce S - LSE/scale and dP - D).
+constexpr int kStatsPerBlock = 64;
 
 struct BwdArgs {
   const __bf16* q;
   const __bf16* k;
   const __bf16* v;
   const __bf16* dout;
-  const float* stats;  // [BH][nqb32][kStatsPerBlock] per 32-row block: LSE*log2(e) x32, -LSE/scale x32, -D x32
+  const __bf16* o;     // forward output O, for D = rowsum(dO o O)
+  const float* lse;    // forward log-sum-exp [BH][Tq]
+  const float* dlse;   // upstream gradient of the LSE [BH][Tq] (or null)
+  float* stats;        // [BH][nqb32][kStatsPerBlock] per 32-row block: -LSE/scale x32, -D x32
   __bf16* dq;
   __bf16* dk;
   __bf16* dv;
@@ -74,51 +77,6 @@ struct BwdArgs {
   int kv_zero_items;                  // dK/dV (causal): some key blocks are past every query
   float scale, scale_log2;
 };
-
-// ---------------------------------------------------------------------------------
-// bwd_stats: 16 lanes per query row (padded to a multiple of 32 rows per head),
-// rows walked with a 64-bit grid stride so that any B*H*Tq the ABI accepts is
-// covered.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_stats_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ dout,
-                                                        const float* __restrict__ lse, const float* __restrict__ dlse,
-                                                        float* __restrict__ stats, int BH, int Tq, int nqb32,
-                                                        float scale) {
-  constexpr int PER = D / 16;
-  const int sub = threadIdx.x % 16;
-  const size_t rows_pad = (size_t)nqb32 * 32;
-  const size_t n_rows = (size_t)BH * rows_pad;
-  const size_t stride = (size_t)gridDim.x * (blockDim.x / 16);
-  // the trip count is uniform across the 16 lanes of a row (a whole row per
-  // 16-lane group), so the shuffles below see all of their lanes
-  for (size_t row = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) / 16; row < n_rows; row += stride) {
-    const size_t bh = row / rows_pad;
-    const int qi = (int)(row % rows_pad);
-    const bool ok = qi < Tq;
-    float acc = 0.f;
-    if (ok) {
-      const size_t base = (bh * Tq + qi) * D + sub * PER;
-      const uint16_t* op = reinterpret_cast<const uint16_t*>(o) + base;
-      const uint16_t* dp = reinterpret_cast<const uint16_t*>(dout) + base;
-#pragma unroll
-      for (int j = 0; j < PER; ++j) acc += bf16_to_f32(op[j]) * bf16_to_f32(dp[j]);
-    }
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
-    if (sub == 0) {
-      float l2 = INFINITY, nl = -INFINITY;
-      if (ok) {
-        const float l = lse[bh * Tq + qi];
-        l2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
-        nl = (l == -INFINITY) ? -INFINITY : -l / scale;
-      }
-      float* blk = stats + (bh * nqb32 + qi / 32) * kStatsPerBlock;
-      blk[qi % 32] = l2;
-      blk[32 + qi % 32] = nl;
-      blk[64 + qi % 32] = ok ? (dlse ? dlse[bh * Tq + qi] : 0.f) - acc : 0.f;
-    }
-  }
-}
 
 // ---------------------------------------------------------------------------------
 // bwd_dkdv: workgroups of 8 waves, each owning 128 keys (an item) at a time
@@ -186,7 +144,7 @@ __device__ __forceinline__ void dkdv_issue(const BwdArgs& a, int bh, int t, __bf
   // 256 bytes of row statistics (-LSE/scale, -D): lanes 0..3 of every
   // gradient wave copy 64 of them
   if (lane < 4) {
-    const float* src = a.stats + ((size_t)bh * a.nqb32 + t) * kStatsPerBlock + 32 + 16 * gw;
+    const float* src = a.stats + ((size_t)bh * a.nqb32 + t) * kStatsPerBlock + 16 * gw;
     dma16_sbase(src, (uint32_t)(16 * lane), stg + 2 * C::TILE + 32 * gw);
   }
 }
@@ -575,6 +533,21 @@ struct DqCfg {
   static_assert(DMA >= 1 && TILE * 2 == DMA * WAVES * 1024, "tile copy split");
 };
 
+// sum over 8 bf16 pairs, in fp32 (products of bf16 values are exact in fp32)
+__device__ __forceinline__ float dot8_bf16(const bf16x8& a, const bf16x8& b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const u32x4 x = __builtin_bit_cast(u32x4, a), y = __builtin_bit_cast(u32x4, b);
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    // copy the element out first: a bit cast of a vector-element lvalue reads
+    // element 0 with this compiler
+    const unsigned xe = x[e], ye = y[e];
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xe), __builtin_bit_cast(bf16x2, ye), s, false);
+  }
+  return s;
+}
+
 struct DqWave {
   bf16x8 qf[8], df[8];  // Q, dO rows of this lane's query as B operands
   f32x16 dqt[4];
@@ -718,17 +691,38 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int cb = 0; cb < C::CB; ++cb) w.dqt[cb] = f32x16{};
-    w.lse2 = INFINITY;
-    w.ndsum = 0.f;
-    if (my_q < a.Tq) {
-      const float* blk = a.stats + ((size_t)bh * a.nqb32 + my_q / 32) * kStatsPerBlock;
-      w.lse2 = blk[my_q % 32];
-      w.ndsum = blk[64 + my_q % 32];
+    // This row's statistics ("Gradient of S": D = ROW_SUM(dO o O), with the
+    // forward's O): lanes l and l+32 hold the two halves of the row's dO and
+    // load the same halves of O.  With an upstream gradient dLSE on the
+    // log-sum-exp, dS gains dLSE_i P_ij, i.e. D becomes D - dLSE.  Split 0
+    // of every query block also writes -LSE/scale and -D for the dK/dV
+    // kernel, launched after this one (rows past Tq: -inf and 0, so that
+    // their P is 0).
+    const __bf16* Oh = a.o + (size_t)bh * a.Tq * D;
+    bf16x8 of[C::KS];
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) of[ks] = ld16(Oh + (size_t)qr * D + 16 * ks + 8 * hf);
+    const bool in = my_q < a.Tq;
+    float l = -INFINITY, dl = 0.f;
+    if (in) {
+      l = a.lse[(size_t)bh * a.Tq + my_q];
+      if (a.dlse) dl = a.dlse[(size_t)bh * a.Tq + my_q];
     }
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       settle(w.qf[ks]);
       settle(w.df[ks]);
+    }
+    float dsum = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) dsum += dot8_bf16(w.df[ks], of[ks]);
+    dsum = pair_sum(dsum);
+    w.lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
+    w.ndsum = in ? dl - dsum : 0.f;
+    if ((!SPLIT || split == 0) && hf == 0 && my_q < a.nqb32 * 32) {
+      float* blk = a.stats + ((size_t)bh * a.nqb32 + my_q / 32) * kStatsPerBlock;
+      blk[my_q % 32] = (l == -INFINITY) ? -INFINITY : -l / a.scale;
+      blk[32 + my_q % 32] = w.ndsum;
     }
     settle(w.lse2);
     settle(w.ndsum);
@@ -843,39 +837,8 @@ BwdLayout bwd_layout(int BH, int Tq, int Tk, int d, int dq_splits) {
 }
 
 template <int D>
-hipError_t bwd_launch_d(BwdArgs& args, const __bf16* o, const float* lse, const float* dlse, bool causal, char* ws,
-                        const BwdLayout& L, hipStream_t stream) {
-  // pre-pass: row statistics
-  prof_begin(2, stream);
-  {
-    // 16 rows per 256-thread block; at most 2^20 blocks, striding beyond
-    const size_t rows = (size_t)args.BH * args.nqb32 * 32;
-    const unsigned blocks = (unsigned)std::min<size_t>((rows + 15) / 16, (size_t)1 << 20);
-    hipLaunchKernelGGL(bwd_stats_kernel<D>, dim3(blocks), dim3(256), 0, stream, o, args.dout, lse, dlse,
-                       reinterpret_cast<float*>(ws + L.stats), args.BH, args.Tq, args.nqb32, args.scale);
-  }
-  prof_end(2, stream);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-
-  const int nkb = (args.Tk + KvCfg<D>::BK - 1) / KvCfg<D>::BK;
-  const int nqt = (args.Tq + 31) / 32;
-  const long long items = causal ? (long long)args.BH * ((nkb + 1) / 2) : (long long)args.BH * nkb;
-  const int resident = causal ? resident_workgroups<bwd_dkdv_kernel<D, true>>(512)
-                              : resident_workgroups<bwd_dkdv_kernel<D, false>>(512);
-  if (resident <= 0) return hipErrorInvalidDevice;
-  args.kv_nkb = nkb;
-  args.kv_nwg = (int)std::min<long long>(items, resident);
-  args.kv_zero_items = causal && (nkb - 1) * (KvCfg<D>::BK / 32) >= nqt;
-  prof_begin(3, stream);
-  if (causal)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(args.kv_nwg), dim3(512), 0, stream, args);
-  else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(args.kv_nwg), dim3(512), 0, stream, args);
-  prof_end(3, stream);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-
+hipError_t bwd_launch_d(BwdArgs& args, bool causal, hipStream_t stream) {
+  // dQ first: it also writes the row statistics the dK/dV kernel reads
   const int nqb = (args.Tq + DqCfg<D>::BM - 1) / DqCfg<D>::BM;
   const int ns = args.dq_splits;
   prof_begin(4, stream);
@@ -895,6 +858,24 @@ hipError_t bwd_launch_d(BwdArgs& args, const __bf16* o, const float* lse, const 
       hipLaunchKernelGGL((bwd_dq_kernel<D, false, false>), grid, dim3(512), 0, stream, args);
   }
   prof_end(4, stream);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  const int nkb = (args.Tk + KvCfg<D>::BK - 1) / KvCfg<D>::BK;
+  const int nqt = (args.Tq + 31) / 32;
+  const long long items = causal ? (long long)args.BH * ((nkb + 1) / 2) : (long long)args.BH * nkb;
+  const int resident = causal ? resident_workgroups<bwd_dkdv_kernel<D, true>>(512)
+                              : resident_workgroups<bwd_dkdv_kernel<D, false>>(512);
+  if (resident <= 0) return hipErrorInvalidDevice;
+  args.kv_nkb = nkb;
+  args.kv_nwg = (int)std::min<long long>(items, resident);
+  args.kv_zero_items = causal && (nkb - 1) * (KvCfg<D>::BK / 32) >= nqt;
+  prof_begin(3, stream);
+  if (causal)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(args.kv_nwg), dim3(512), 0, stream, args);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(args.kv_nwg), dim3(512), 0, stream, args);
+  prof_end(3, stream);
   return hipGetLastError();
 }
 
@@ -927,7 +908,10 @@ hipError_t bwd_bf16_launch(const void* q, const void* k, const void* v, const vo
   a.k = static_cast<const __bf16*>(k);
   a.v = static_cast<const __bf16*>(v);
   a.dout = static_cast<const __bf16*>(dout);
-  a.stats = reinterpret_cast<const float*>(ws + L.stats);
+  a.o = static_cast<const __bf16*>(o);
+  a.lse = lse;
+  a.dlse = dlse;
+  a.stats = reinterpret_cast<float*>(ws + L.stats);
   a.dq = static_cast<__bf16*>(dq);
   a.dk = static_cast<__bf16*>(dk);
   a.dv = static_cast<__bf16*>(dv);
@@ -942,9 +926,7 @@ hipError_t bwd_bf16_launch(const void* q, const void* k, const void* v, const vo
   a.dq_part = sp.splits > 1 ? reinterpret_cast<float*>(ws + L.dq_part) : nullptr;
   a.scale = scale;
   a.scale_log2 = scale * kLog2e;
-  const __bf16* ob = static_cast<const __bf16*>(o);
-  return d == 128 ? bwd_launch_d<128>(a, ob, lse, dlse, causal != 0, ws, L, stream)
-                  : bwd_launch_d<64>(a, ob, lse, dlse, causal != 0, ws, L, stream);
+  return d == 128 ? bwd_launch_d<128>(a, causal != 0, stream) : bwd_launch_d<64>(a, causal != 0, stream);
 }
 
 // ---- scratch memory of the entry point that allocates nothing -------------------

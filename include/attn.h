@@ -149,8 +149,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
  *   partials fit, else the largest that fits (the summation order of dQ, and
  *   so its last bits, can then differ from attn_bwd's).
  *   ATTN_ERR_TOO_LARGE (checked before any HIP call) when not even the row
- *   statistics fit: about B*H*Tq*12 bytes, i.e. B*H*Tq above about 5.6
- *   million rows.  The first call on a device looks up the device address of that
+ *   statistics fit: about B*H*Tq*8 bytes, i.e. B*H*Tq above about 8.4 million
+ *   rows.  The first call on a device looks up the device address of that
  *   device's copy (hipGetSymbolAddress) and keeps it.
  *   Calls on one GPU share its scratch: two calls whose work overlaps in time
  *   on one GPU (different streams, or host threads) race and corrupt each
@@ -322,7 +322,7 @@ int attn_bwd_f32(const float* q, const float* k, const float* v, const float* o,
  */
 #define ATTN_KERNEL_FWD 0            /* forward main kernel */
 #define ATTN_KERNEL_FWD_AUX 1        /* forward: merge of key-split states (attn_fwd, attn_decode) */
-#define ATTN_KERNEL_BWD_PREP 2       /* D = rowsum(dO o O) (- dLSE), LSE*log2(e) */
+#define ATTN_KERNEL_BWD_PREP 2       /* (no longer launched: the dQ kernel forms the row statistics) */
 #define ATTN_KERNEL_BWD_DKDV 3       /* backward: dK and dV */
 #define ATTN_KERNEL_BWD_DQ 4         /* backward: dQ */
 #define ATTN_KERNEL_DECODE 5         /* decode main kernel (its split merge counts as ATTN_KERNEL_FWD_AUX) */
