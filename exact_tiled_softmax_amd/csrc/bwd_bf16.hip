@@ -583,7 +583,7 @@ __device__ __forceinline__ void dq_softmax(const BwdArgs& a, const DqWave& w, co
       const int kk = key0 + 8 * (r / 4) + 4 * hf + (r % 4);
       p = ((CAUSAL && kk > my_q) || kk >= a.Tk) ? 0.f : p;
     }
-    db[r / 8][r % 8] = to_bf16(p * (dpt[r] + w.ndsum));
+    db[r / 8][r % 8] = to_bf16(p * dpt[r]);  // dP^T - D: the accumulator started at -D
   }
 }
 
@@ -626,7 +626,9 @@ __device__ __forceinline__ void dq_compute(const BwdArgs& a, DqWave& w, const __
     };
 #pragma unroll
     for (int ks = 0; ks < LA; ++ks) rd(ks);
-    f32x16 st = {}, dpt = {};
+    f32x16 st = {}, dpt;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dpt[r] = w.ndsum;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       __builtin_amdgcn_sched_barrier(0);
