@@ -96,7 +96,8 @@ struct FwdArgs {
   int BH, Tq, Tk, Tk_pad;
   int diag;          // causal: key j is blocked for query i when j > i + diag
   int num_qtiles, num_splits, keys_per_split;
-  int n_items;       // BH * num_qtiles * num_splits
+  int n_items;         // BH * num_qtiles * num_splits
+  int n_items_paired;  // BH * ceil(num_qtiles / 2) * num_splits: pairs of query tiles
   int nwg;           // workgroups of the persistent launch
   float scale_log2;  // scale * log2(e)
 };
@@ -272,12 +273,12 @@ __device__ __forceinline__ void fwd_tile(const char* stg, const FwdLdsOffsets<D>
 // workgroup waits on the dispatcher between items (with one workgroup per CU
 // a CU idled about 6 us, median, between two workgroups), and the first tile
 // copies of the next item are issued before the current item's outputs are
-// written.  Items are dealt round-robin (item wg + r*nwg in head-major order,
-// query tile fastest): one XCD's workgroups (consecutive logical ids,
-// xcd_remap) hold the query tiles of one or two heads in each round and share
-// their K/V tiles in L2.  Odd rounds take a head's query tiles in reverse
-// order, so that a workgroup's causal work (query tile j, then nq-1-j) evens
-// out over two rounds.
+// written.  Items come in pairs (query tile nq-1-k, query tile k) of one
+// (head, split), whose causal work adds up to the same total for every k,
+// dealt round-robin over the workgroups (pair wg + r*nwg, head-major): one
+// XCD's workgroups (consecutive logical ids, xcd_remap) hold the pairs of one
+// or two heads in each round and share their K/V tiles in L2.  With no more
+// items than workgroups, each workgroup takes one item.
 struct FwdItem {
   int bh, qt, split;
   int kbeg, kend, ntiles;  // key range and its 64-key tiles
@@ -287,12 +288,29 @@ template <int D, bool CAUSAL, bool SPLIT>
 __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int wg, int m, FwdItem& it) {
   using C = FwdCfg<D>;
   const int nq = a.num_qtiles;
-  const int i = wg + m * a.nwg;
-  if (i >= a.n_items) return false;
-  const int j = i % nq, rest = i / nq;
+  int rest;
+  if (a.nwg >= a.n_items) {
+    // one item per workgroup, query tile fastest
+    if (m > 0 || wg >= a.n_items) return false;
+    rest = wg / nq;
+    it.qt = wg % nq;
+  } else {
+    // pairs (query tile nq-1-k, query tile k) of one (head, split), dealt
+    // round-robin; the middle tile of an odd count pairs with itself and is
+    // run once
+    const int npair = (nq + 1) >> 1;
+    const int q = wg + (m >> 1) * a.nwg;
+    if (q >= a.n_items_paired) return false;
+    rest = q / npair;
+    const int k = q - rest * npair;
+    if ((m & 1) && nq - 1 - k == k) {
+      it.ntiles = -1;  // the middle tile, already run
+      return true;
+    }
+    it.qt = (m & 1) ? k : nq - 1 - k;
+  }
   it.split = SPLIT ? rest % a.num_splits : 0;
   it.bh = SPLIT ? rest / a.num_splits : rest;
-  it.qt = (m & 1) ? nq - 1 - j : j;
   int kbeg = 0, kend = a.Tk;
   if (SPLIT) {
     kbeg = it.split * a.keys_per_split;
@@ -345,10 +363,18 @@ __global__ __launch_bounds__(FwdCfg<D>::THREADS, FwdCfg<D>::WAVES_PER_SIMD) void
   const FwdLdsOffsets<D> lo = fwd_lds_offsets<D>(lane);
   const float c = a.scale_log2;
 
+  // item m of the workgroup's list, or the first after it that is not a
+  // repeated middle tile (m advances to it); false at the end of the list
+  auto take = [&](int& m, FwdItem& it) {
+    for (; fwd_item<D, CAUSAL, SPLIT>(a, wg, m, it); ++m)
+      if (it.ntiles >= 0) return true;
+    return false;
+  };
   FwdItem it;
-  bool have = fwd_item<D, CAUSAL, SPLIT>(a, wg, 0, it);
+  int m = 0;
+  bool have = take(m, it);
   if (have) prologue(it);
-  for (int m = 0; have; ++m) {
+  while (have) {
     const int q0 = it.qt * C::BM;
     const int row = q0 + wave * 32 + lr;  // this lane's query row
     const int ntiles = it.ntiles, kbeg = it.kbeg, kend = it.kend;
@@ -405,7 +431,8 @@ __global__ __launch_bounds__(FwdCfg<D>::THREADS, FwdCfg<D>::WAVES_PER_SIMD) void
     // every wave is done with the stages once all have passed this barrier
     const FwdItem cur = it;
     if constexpr (C::PERSIST) {
-      have = fwd_item<D, CAUSAL, SPLIT>(a, wg, m + 1, it);
+      ++m;
+      have = take(m, it);
       barrier();
       if (have) prologue(it);
     } else {
@@ -491,7 +518,7 @@ template <int D, bool CAUSAL, bool SPLIT>
 hipError_t launch_fwd(FwdArgs args, hipStream_t stream) {
   const int resident = resident_workgroups<fwd_bf16_kernel<D, CAUSAL, SPLIT>>(FwdCfg<D>::THREADS);
   if (resident <= 0) return hipErrorInvalidDevice;
-  args.nwg = FwdCfg<D>::PERSIST ? std::min(args.n_items, resident) : args.n_items;
+  args.nwg = (FwdCfg<D>::PERSIST && args.n_items > resident) ? std::min(args.n_items_paired, resident) : args.n_items;
   prof_begin(0, stream);
   hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, SPLIT>), dim3(args.nwg), dim3(FwdCfg<D>::THREADS), 0, stream, args);
   prof_end(0, stream);
@@ -575,6 +602,7 @@ FwdArgs fwd_args(const void* q, const void* k, const void* v, void* o, float* ls
   const int kblocks = (Tk + kBN - 1) / kBN;
   args.keys_per_split = ((kblocks + num_splits - 1) / num_splits) * kBN;
   args.n_items = BH * args.num_qtiles * num_splits;
+  args.n_items_paired = BH * ((args.num_qtiles + 1) / 2) * num_splits;
   args.scale_log2 = scale * kLog2e;
   return args;
 }

@@ -315,10 +315,10 @@ def test_bf16_scale_zero_gives_mean_of_allowed_values(dev):
 
 
 # Without the causal mask and with few query tiles, one dK/dV workgroup walks
-# several consecutive key blocks of a head (the query-tile stream runs on
-# across them).  64 heads keep the launch large enough for the walk to be
-# chosen; ragged key counts leave a short last block and a workgroup with
-# fewer blocks than the others.
+# Few query tiles against many key blocks, without the causal mask: every
+# dK/dV workgroup runs several key blocks (of one head or across heads) as
+# one stream of query tiles; ragged key counts leave a short last block and
+# workgroups with fewer blocks than the others.
 @pytest.mark.parametrize("shape", [(1, 64, 64, 2048, 128, 128),   # 2 key blocks per workgroup
                                    (1, 128, 40, 1700, 128, 128),  # 3 per workgroup, the last one 2, last block 36 keys
                                    (2, 64, 33, 1000, 64, 64)])    # 2 per workgroup, last block 104 keys
@@ -332,3 +332,29 @@ def test_bf16_bwd_key_block_walk(dev, shape):
     assert_close("dQ", f64(dq), rq, TOL_BF16)
     assert_close("dK", f64(dk), rk, TOL_BF16)
     assert_close("dV", f64(dv), rv, TOL_BF16)
+
+
+# Lists of several items per persistent workgroup (the dK/dV launch and the
+# d = 128 forward hold one workgroup per CU): more causal key-block pairs than
+# workgroups, an odd key-block count (the middle block pairs with itself),
+# key blocks that no query reaches (Tk > Tq), single-tile items (Tq <= 32),
+# and heads crossing between consecutive items of a workgroup.
+@pytest.mark.parametrize("shape,causal", [((1, 96, 600, 600, 128, 128), True),
+                                          ((1, 64, 300, 1100, 128, 128), True),
+                                          ((1, 160, 20, 900, 128, 128), True),
+                                          ((2, 72, 300, 900, 64, 64), False)])
+def test_bf16_persistent_item_lists(dev, shape, causal):
+    q, k, v, do = bf16_problem(shape, seed=17)
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    o, lse = attn.fwd(qd, kd, vd, causal=causal)
+    dq, dk, dv = attn.bwd(qd, kd, vd, o, lse, dod, causal=causal)
+    torch.cuda.synchronize()
+    scale = 1 / np.sqrt(shape[4])
+    ro, rl = dense_forward(f64(q), f64(k), f64(v), scale, causal)
+    assert_close(f"O {shape} causal={causal}", f64(o), ro, TOL_BF16)
+    assert_close("LSE", f64(lse), rl, TOL_LSE_BF16)
+    rq, rk, rv = dense_backward(f64(q), f64(k), f64(v), f64(do), scale, causal)
+    assert_close("dQ", f64(dq), rq, TOL_BF16)
+    assert_close("dK", f64(dk), rk, TOL_BF16)
+    assert_close("dV", f64(dv), rv, TOL_BF16)
+
