@@ -52,18 +52,6 @@ __device__ __forceinline__ void barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n
 
 __device__ __forceinline__ bf16x8 ld16(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
-// A 16-byte LDS read that the compiler can neither move nor merge: the read
-// and the wait for it are one asm statement.  For rare reads on a branch,
-// which the compiler would otherwise hoist above it.
-__device__ __forceinline__ bf16x8 lds_read16_now(const char* p) {
-  u32x4 r;
-  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)"
-               : "=v"(r)
-               : "v"(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_cvoid*)p)))
-               : "memory");
-  return __builtin_bit_cast(bf16x8, r);
-}
-
 // Make the compiler complete a register load here, before the tile copies
 // that follow are issued: its own waits count only its own loads, so a wait
 // for this value inside the tile loop would also drain the copies.
