@@ -107,6 +107,10 @@ struct FwdArgs {
 template <int D>
 __device__ __forceinline__ void fwd_issue(const FwdArgs& a, int bh, int key0, __bf16* stg, int wave, int lane) {
   using C = FwdCfg<D>;
+  // The lane index is made opaque here: otherwise the compiler hoists this
+  // rare path's per-lane 64-bit addresses out of the tile loop and keeps them
+  // in registers for the whole kernel (22 VGPRs at head dim 128).
+  asm volatile("" : "+v"(lane));
   const __bf16* Kh = a.k + (size_t)bh * a.Tk * D;
   const __bf16* Vh = a.v + (size_t)bh * a.Tk * D;
 #pragma unroll
