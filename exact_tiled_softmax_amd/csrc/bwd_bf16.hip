@@ -533,19 +533,21 @@ struct DqCfg {
   static_assert(DMA >= 1 && TILE * 2 == DMA * WAVES * 1024, "tile copy split");
 };
 
-// sum over 8 bf16 pairs, in fp32 (products of bf16 values are exact in fp32)
-__device__ __forceinline__ float dot8_bf16(const bf16x8& a, const bf16x8& b) {
+// acc + the sum over 8 bf16 pairs, in fp32, as one chain of dot products in
+// a fixed order (the running sum is each step's accumulator, so that the
+// compiler has no additions of its own to contract differently from one
+// build to the next)
+__device__ __forceinline__ float dot8_bf16(const bf16x8& a, const bf16x8& b, float acc) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const u32x4 x = __builtin_bit_cast(u32x4, a), y = __builtin_bit_cast(u32x4, b);
-  float s = 0.f;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     // copy the element out first: a bit cast of a vector-element lvalue reads
     // element 0 with this compiler
     const unsigned xe = x[e], ye = y[e];
-    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xe), __builtin_bit_cast(bf16x2, ye), s, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xe), __builtin_bit_cast(bf16x2, ye), acc, false);
   }
-  return s;
+  return acc;
 }
 
 struct DqWave {
@@ -717,7 +719,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdArgs a) {
     }
     float dsum = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) dsum += dot8_bf16(w.df[ks], of[ks]);
+    for (int ks = 0; ks < C::KS; ++ks) dsum = dot8_bf16(w.df[ks], of[ks], dsum);
     dsum = pair_sum(dsum);
     w.lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
     w.ndsum = in ? dl - dsum : 0.f;
