@@ -20,6 +20,53 @@
 namespace attn {
 namespace {
 
+// Row of a 16-row group that the transposed copies store at position p
+// (0..15).  An MFMA accumulator gives lane half h the rows 4h..4h+3 and
+// 8+4h..8+4h+3 of each 16-row group, and an operand read takes 8 consecutive
+// positions, so position 8h+e holds row (e < 4 ? 4h+e : 8+4h+e-4).
+__device__ __forceinline__ int group_row(int p) {
+  const int h = (p >> 3) & 1, e = p & 7;
+  return (e < 4) ? 4 * h + e : 8 + 4 * h + (e - 4);
+}
+
+// Transposed copy [d][Tpad] of a row-major [T][d] bf16 tensor (per head),
+// rows of each 16-row group stored in group_row order, zero past T.
+// One 64-row block of one head per workgroup.
+// out[bh][c][tpos] = in[bh][t][c] with t = 16*(tpos/16) + group_row(tpos%16),
+// zero for t >= T.
+template <int D>
+__global__ __launch_bounds__(256) void transpose_rows_kernel(const __bf16* __restrict__ in_all,
+                                                            __bf16* __restrict__ out_all, int T, int Tpad) {
+  constexpr int STR = D + 8;
+  constexpr int CPR = D / 8;
+  __shared__ __attribute__((aligned(16))) __bf16 tile[64 * STR];
+  const int bh = blockIdx.y;
+  const int t0 = blockIdx.x * 64;
+  const __bf16* in = in_all + (size_t)bh * T * D;
+  __bf16* out = out_all + (size_t)bh * D * Tpad;
+  for (int c = threadIdx.x; c < 64 * CPR; c += 256) {
+    const int r = c / CPR, col = (c % CPR) * 8;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (t0 + r < T) x = *reinterpret_cast<const u32x4*>(in + (size_t)(t0 + r) * D + col);
+    *reinterpret_cast<u32x4*>(tile + r * STR + col) = x;
+  }
+  __syncthreads();
+  const uint16_t* ts = reinterpret_cast<const uint16_t*>(tile);
+  for (int it = threadIdx.x; it < D * 8; it += 256) {
+    const int c = it / 8, m = it % 8;  // output row c, positions 8m..8m+7
+    unsigned w[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const int p0 = 8 * m + e, p1 = p0 + 1;
+      const int r0 = (p0 & ~15) + group_row(p0 & 15), r1 = (p1 & ~15) + group_row(p1 & 15);
+      w[e / 2] = (unsigned)ts[r0 * STR + c] | ((unsigned)ts[r1 * STR + c] << 16);
+    }
+    const u32x4 v = {w[0], w[1], w[2], w[3]};
+    *reinterpret_cast<u32x4*>(out + (size_t)c * Tpad + t0 + 8 * m) = v;
+  }
+}
+
+
 constexpr int kStdWaves = 4;                // one wave = 32 query rows
 constexpr int kStdRows = 32 * kStdWaves;    // query rows per workgroup
 
