@@ -252,10 +252,8 @@ def bench_decode(args, w, cpu) -> int:
         attn.decode(q, k, v, kv_lens=lens, scale=w.scale, causal=w.causal, out=o, lse=lse,
                     num_splits=args.decode_splits or None)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
+    n_warm = warm_up(step, args.warmup, args.warmup_min_s)
+    print(f"[bench] warmup done ({n_warm} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
     attn.profile_start()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -290,6 +288,8 @@ def bench_decode(args, w, cpu) -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_min_s": args.warmup_min_s,
+        "warmup_steps_run": n_warm,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -318,7 +318,9 @@ def standard_bytes(w):
 
 def bench_standard(args, w) -> int:
     """The IO comparison: the tiled forward and the materialised standard
-    forward timed on the same inputs, one after the other."""
+    forward timed on the same inputs, one after the other.  The compared
+    times are the kernels' own (the library's HIP events); wall times per
+    call are reported beside them."""
     import torch
 
     from exact_tiled_softmax_amd import attn
@@ -329,17 +331,25 @@ def bench_standard(args, w) -> int:
     q, k, v = (make_tensor(w, n).to(dev) for n in ("q", "k", "v"))
     o = torch.empty((w.B, w.H, w.Tq, w.dv), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.B, w.H, w.Tq), dtype=torch.float32, device=dev)
-    res = {}
+    res, wall = {}, {}
+    kinds = {"tiled": ("fwd", "fwd_aux"), "standard": ("standard",)}
     for name, fn in (("tiled", attn.fwd), ("standard", attn.fwd_standard)):
-        for _ in range(args.warmup):
-            fn(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse)
+        warm_up(lambda: fn(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse), args.warmup, args.warmup_min_s)
+        attn.profile_start()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(args.steps):
             fn(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse)
         torch.cuda.synchronize()
-        res[name] = (time.perf_counter() - t0) * 1e3 / args.steps
-        print(f"[bench] {name}: {res[name]:.3f} ms per call", file=sys.stderr, flush=True)
+        wall[name] = (time.perf_counter() - t0) * 1e3 / args.steps
+        attn.profile_stop()
+        # kernel time from the library's HIP events: the wall time of the
+        # standard path also holds the mapping of its workspace, which the
+        # driver sometimes takes hundreds of ms over
+        res[name] = sum(attn.profile_query(kind)[0] for kind, n in attn.KERNEL_NAMES.items()
+                        if n in kinds[name]) / args.steps
+        print(f"[bench] {name}: {res[name]:.3f} ms of kernels, {wall[name]:.3f} ms wall per call", file=sys.stderr,
+              flush=True)
     _, fwd_fl, _, fwd_b, _ = work(w)
     std_b = standard_bytes(w)
     line = {
@@ -349,6 +359,7 @@ def bench_standard(args, w) -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_min_s": args.warmup_min_s,
         "ms_per_step": round(res["standard"], 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -360,6 +371,8 @@ def bench_standard(args, w) -> int:
         "io_comparison": {
             "tiled_ms": round(res["tiled"], 4),
             "standard_ms": round(res["standard"], 4),
+            "tiled_wall_ms": round(wall["tiled"], 4),
+            "standard_wall_ms": round(wall["standard"], 4),
             "standard_over_tiled_time": round(res["standard"] / res["tiled"], 2),
             "tiled_algorithmic_bytes": fwd_b,
             "standard_hbm_bytes_model": std_b,
@@ -371,7 +384,26 @@ def bench_standard(args, w) -> int:
     return 0
 
 
-def time_steps(attn, w, dev, steps, warmup, flush_mib=0):
+def warm_up(step, steps, min_s):
+    """Run `step` at least `steps` times and, beyond that, until at least
+    `min_s` seconds of back-to-back work have run.  From idle the GPU's clock
+    takes longer than a few short steps to reach its loaded level: five
+    warm-up steps of the L=4096 workload (3.4 ms) left its kernels 14% slower
+    than after 200.  Returns the number of warm-up steps run."""
+    import torch
+
+    n = 0
+    t0 = time.perf_counter()
+    while n < steps or time.perf_counter() - t0 < min_s:
+        step()
+        n += 1
+        if n >= steps:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
+def time_steps(attn, w, dev, steps, warmup, flush_mib=0, warmup_min_s=0.0):
     """Warm up, then time `steps` fwd+bwd steps of workload w with inputs
     resident on `dev`.  Returns ({kernel: (total_ms, launches)} from the
     library's HIP events, wall ms per step).  With flush_mib > 0 a buffer of
@@ -394,10 +426,8 @@ def time_steps(attn, w, dev, steps, warmup, flush_mib=0):
         attn.fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse)
         attn.bwd(q, k, v, o, lse, do, scale=w.scale, causal=w.causal, dq=dq, dk=dk, dv=dvg)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    print(f"[bench] {w.name}: warmup done ({warmup} steps); timing {steps} steps", file=sys.stderr, flush=True)
+    n_warm = warm_up(step, warmup, warmup_min_s)
+    print(f"[bench] {w.name}: warmup done ({n_warm} steps); timing {steps} steps", file=sys.stderr, flush=True)
     attn.profile_start()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -411,7 +441,7 @@ def time_steps(attn, w, dev, steps, warmup, flush_mib=0):
     if flush is not None:
         # the flush between steps is not attention work
         ms_step = sum(kern[n][0] for n in ("fwd", "fwd_aux", "bwd_prep", "bwd_dkdv", "bwd_dq")) / steps
-    return kern, ms_step
+    return kern, ms_step, n_warm
 
 
 def main(argv=None) -> int:
@@ -419,6 +449,9 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup-min-s", type=float, default=0.5, metavar="S",
+                    help="keep warming up past --warmup steps until S seconds of back-to-back steps have run "
+                         "(the GPU clock needs that long to leave its idle level)")
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle work (0 = skip)")
     ap.add_argument("--flush-mib", type=int, default=0, metavar="MIB",
@@ -474,7 +507,7 @@ def main(argv=None) -> int:
     if args.standard:
         return bench_standard(args, w)
     dev = torch.device("cuda:0")
-    kern, ms_step = time_steps(attn, w, dev, args.steps, args.warmup, args.flush_mib)
+    kern, ms_step, n_warm = time_steps(attn, w, dev, args.steps, args.warmup, args.flush_mib, args.warmup_min_s)
     pairs, fwd_fl, bwd_fl, fwd_b, bwd_b = work(w)
     fwd_ms = (kern["fwd"][0] + kern["fwd_aux"][0]) / args.steps
     bwd_ms = (kern["bwd_prep"][0] + kern["bwd_dkdv"][0] + kern["bwd_dq"][0]) / args.steps
@@ -512,7 +545,7 @@ def main(argv=None) -> int:
                         "bwd_frac_of_peak": round(bwd_tflops / PEAK_BF16_TFLOPS, 4) if bwd_tflops else None}}
     if args.targets and w.name == HEADLINE:
         wt = WORKLOADS[BWD_TARGET]
-        kt, _ = time_steps(attn, wt, dev, args.steps, args.warmup, args.flush_mib)
+        kt, _, t_warm = time_steps(attn, wt, dev, args.steps, args.warmup, args.flush_mib, args.warmup_min_s)
         _, tf_fl, tb_fl, _, _ = work(wt)
         t_fwd_ms = (kt["fwd"][0] + kt["fwd_aux"][0]) / args.steps
         t_bwd_ms = (kt["bwd_prep"][0] + kt["bwd_dkdv"][0] + kt["bwd_dq"][0]) / args.steps
@@ -521,6 +554,7 @@ def main(argv=None) -> int:
             "fwd_frac_of_peak": round(tf_fl / (t_fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "bwd_ms": round(t_bwd_ms, 4),
             "bwd_frac_of_peak": round(tb_fl / (t_bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "warmup_steps_run": t_warm,
             "kernel_ms_per_step": {n: round(kt[n][0] / args.steps, 4) for n in kt if kt[n][1]},
         }
 
@@ -531,6 +565,8 @@ def main(argv=None) -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_min_s": args.warmup_min_s,
+        "warmup_steps_run": n_warm,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",

@@ -45,6 +45,52 @@ int check_common(const void* q, const void* k, const void* v, const void* o, con
 
 bool bf16_dims_supported(int d, int dv) { return d == dv && (d == 64 || d == 128); }
 
+// Workspace memory.  Every call takes its workspace stream-ordered from a
+// memory pool that the library creates per device and that keeps up to
+// kPoolKeepBytes of freed memory across synchronisations.  (The device's
+// default pool hands freed memory back to the driver whenever the device
+// synchronises, and the next allocation maps fresh memory: with the device
+// synchronised after every call, a backward of B=2 H=32 L=8192 took about
+// 75 us longer than back to back; from this pool, about 10 us.)  Pools live
+// until the process ends.
+constexpr uint64_t kPoolKeepBytes = 256ull << 20;
+std::mutex g_pool_mu;
+std::vector<hipMemPool_t> g_pools;  // by device ordinal, null until first use
+
+hipError_t ws_pool(hipMemPool_t* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_pool_mu);
+  if ((int)g_pools.size() <= dev) g_pools.resize(dev + 1, nullptr);
+  if (!g_pools[dev]) {
+    hipMemPoolProps props = {};
+    props.allocType = hipMemAllocationTypePinned;
+    props.handleTypes = hipMemHandleTypeNone;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t pool = nullptr;
+    e = hipMemPoolCreate(&pool, &props);
+    if (e != hipSuccess) return e;
+    uint64_t keep = kPoolKeepBytes;
+    e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+    if (e != hipSuccess) {
+      (void)hipMemPoolDestroy(pool);
+      return e;
+    }
+    g_pools[dev] = pool;
+  }
+  *out = g_pools[dev];
+  return hipSuccess;
+}
+
+hipError_t ws_alloc(void** ptr, size_t bytes, hipStream_t s) {
+  hipMemPool_t pool = nullptr;
+  hipError_t e = ws_pool(&pool);
+  if (e != hipSuccess) return e;
+  return hipMallocFromPoolAsync(ptr, bytes, pool, s);
+}
+
 int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Tq, int Tk, int d,
              int dv, float scale, int causal, int num_splits, void* stream) {
   int rc = check_common(q, k, v, o, lse, B, H, Tq, Tk, d, dv, scale);
@@ -57,7 +103,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
   const size_t ws_bytes = attn::fwd_bf16_workspace_bytes(BH, Tq, Tk, d, splits);
   void* ws = nullptr;
   if (ws_bytes) {
-    hipError_t e = hipMallocAsync(&ws, ws_bytes, s);
+    hipError_t e = ws_alloc(&ws, ws_bytes, s);
     if (e != hipSuccess) return hip_fail(e);
   }
   hipError_t e = attn::fwd_bf16_launch(q, k, v, o, lse, BH, Tq, Tk, d, scale, causal, splits, ws, s);
@@ -79,7 +125,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
   const int BH = B * H;
   const int splits = attn::bwd_bf16_dq_splits(BH, Tq, Tk, d, SIZE_MAX);
   void* ws = nullptr;
-  hipError_t e = hipMallocAsync(&ws, attn::bwd_bf16_workspace_bytes(BH, Tq, Tk, d, splits), s);
+  hipError_t e = ws_alloc(&ws, attn::bwd_bf16_workspace_bytes(BH, Tq, Tk, d, splits), s);
   if (e != hipSuccess) return hip_fail(e);
   e = attn::bwd_bf16_launch(q, k, v, o, lse, dlse, dout, dq, dk, dv_grad, BH, Tq, Tk, d, scale, causal, splits, ws,
                             s);
@@ -120,7 +166,7 @@ int decode_impl(const void* q, const void* k, const void* v, const int* kv_lens,
   const size_t ws_bytes = attn::decode_bf16_workspace_bytes(BH, Tq, d, splits);
   void* ws = nullptr;
   if (ws_bytes) {
-    hipError_t e = hipMallocAsync(&ws, ws_bytes, s);
+    hipError_t e = ws_alloc(&ws, ws_bytes, s);
     if (e != hipSuccess) return hip_fail(e);
   }
   hipError_t e = attn::decode_bf16_launch(q, k, v, kv_lens, o, lse, B, H, Tq, Tk, d, scale, causal, splits, ws, s);
@@ -297,7 +343,7 @@ int attn_fwd_standard(const void* q, const void* k, const void* v, void* o, floa
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int BH = B * H;
   void* ws = nullptr;
-  hipError_t e = hipMallocAsync(&ws, attn::std_bf16_workspace_bytes(BH, Tq, Tk, d), s);
+  hipError_t e = ws_alloc(&ws, attn::std_bf16_workspace_bytes(BH, Tq, Tk, d), s);
   if (e != hipSuccess) return hip_fail(e);
   e = attn::std_bf16_launch(q, k, v, o, lse, BH, Tq, Tk, d, scale, causal, ws, s);
   hipError_t f = hipFreeAsync(ws, s);

@@ -58,10 +58,13 @@
  *           enqueue work on it and never synchronise; kernel faults surface at
  *           the caller's next synchronisation on that stream.
  * Workspace. Some calls need scratch memory (row statistics of the
- *           backward, split partial states).  The library
- *           takes it with hipMallocAsync on `stream` and returns it with
- *           hipFreeAsync on the same stream, so its lifetime is
- *           stream-ordered and no state persists between calls.
+ *           backward, split partial states).  The library takes it with
+ *           hipMallocFromPoolAsync on `stream` from a memory pool of its own
+ *           (one per device, created at the first such call, kept until the
+ *           process ends, caching up to 256 MiB of freed memory across
+ *           synchronisations) and returns it with hipFreeAsync on the same
+ *           stream, so its lifetime is stream-ordered and no data persists
+ *           between calls.
  * Errors.   Return 0 on success or a negative ATTN_ERR_* code.  Argument
  *           checks happen before any HIP call, so an invalid call has no
  *           effect.  No C++ exception crosses this interface.
@@ -127,8 +130,8 @@ int attn_fwd_splits(const void* q, const void* k, const void* v, void* o, float*
  * element is summed in a fixed order by one workgroup: results are
  * deterministic.  Workspace (row statistics, about B*H*Tq*8 bytes, and,
  * when the dQ kernel splits the key range because there are few query
- * blocks, fp32 partial dQ of splits*B*H*Tq*d*4 bytes) is allocated with
- * hipMallocAsync on `stream`.
+ * blocks, fp32 partial dQ of splits*B*H*Tq*d*4 bytes) comes from the
+ * library's workspace pool on `stream` (see Workspace above).
  * Supported: d == dv, d in {64, 128}; otherwise ATTN_ERR_UNSUPPORTED.
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -230,7 +233,8 @@ int attn_merge_states(const float* acc, const float* m, const float* l, int n, v
  * Same arguments, outputs and supported sizes as attn_fwd; the results agree
  * with attn_fwd to bf16 rounding.  For measuring what the tiled method saves:
  * it takes a workspace of about B*H*Tq*Tk*6 bytes (S in fp32 and P in bf16)
- * from hipMallocAsync on `stream` (ATTN_ERR_HIP if that fails) and moves
+ * from the library's workspace pool on `stream` (ATTN_ERR_HIP if that
+ * fails) and moves
  * Tq*Tk*12 bytes per head through HBM.
  */
 int attn_fwd_standard(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -257,7 +261,7 @@ int attn_fwd_standard(const void* q, const void* k, const void* v, void* o, floa
  * ATTN_ERR_UNSUPPORTED.  The key range is split over workgroups; with more
  * than one split the partial states are merged with the rescale rule
  * ("Chunk-wise Mode with Online Softmax Re-scale"), using a workspace of
- * splits*B*H*Tq*(dv+2) floats from hipMallocAsync on `stream`.
+ * splits*B*H*Tq*(dv+2) floats from the library's workspace pool on `stream`.
  */
 #define ATTN_DECODE_MAX_QUERIES 4
 int attn_decode(const void* q, const void* k, const void* v, const int* kv_lens, void* o, float* lse,
