@@ -40,6 +40,9 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 HEADLINE = "causal_bf16_b2h32_t8192_d128"
 BWD_TARGET = "bwd_causal_bf16_b2h16_t4096_d128"  # the causal backward workload reported beside it
+# further workloads timed beside the headline: head dim 64 (non-causal) and
+# few queries against a long key range
+SIDE_TARGETS = ("fwd_bf16_b4h16_t2048_d64", "longkv_bf16_b1h64_tq256_tk65536_d128")
 METRIC = "attention TFLOP/s fwd & fwd+bwd, bf16 d=128 L=8192 causal; % of MFMA peak"
 
 
@@ -466,7 +469,8 @@ def main(argv=None) -> int:
     ap.add_argument("--decode-splits", type=int, default=0,
                     help="decode workloads: key-range splits per sequence (0 = the library's choice)")
     ap.add_argument("--no-targets", dest="targets", action="store_false",
-                    help="headline workload only: skip timing the L=4096 causal backward workload in the same run")
+                    help="headline workload only: skip timing the L=4096 causal, d=64 and long-key workloads in "
+                         "the same run")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -540,11 +544,12 @@ def main(argv=None) -> int:
         "traffic_over_algorithmic_bytes": round(traffic / kby[dom], 3) if traffic else None,
     }
 
-    # the backward target workload, timed in the same run with the same step counts
+    # the backward target workload and the side workloads, timed in the same
+    # run with the same step counts (inputs of each freed before the next)
     targets = {w.name: {"fwd_frac_of_peak": round(fwd_tflops / PEAK_BF16_TFLOPS, 4) if fwd_tflops else None,
                         "bwd_frac_of_peak": round(bwd_tflops / PEAK_BF16_TFLOPS, 4) if bwd_tflops else None}}
-    if args.targets and w.name == HEADLINE:
-        wt = WORKLOADS[BWD_TARGET]
+    for tname in ((BWD_TARGET,) + SIDE_TARGETS if args.targets and w.name == HEADLINE else ()):
+        wt = WORKLOADS[tname]
         kt, _, t_warm = time_steps(attn, wt, dev, args.steps, args.warmup, args.flush_mib, args.warmup_min_s)
         _, tf_fl, tb_fl, _, _ = work(wt)
         t_fwd_ms = (kt["fwd"][0] + kt["fwd_aux"][0]) / args.steps
