@@ -387,6 +387,96 @@ def bench_standard(args, w) -> int:
     return 0
 
 
+def bench_states(args, w) -> int:
+    """Forward through key-range states (the chunk-wise mode's state and its
+    rescale merge, P1 "Chunk-wise Mode with Online Softmax Re-scale"): the
+    key range is cut into N equal ranges, attn_fwd_state computes each
+    range's partial state (acc, m, l) into one stacked buffer, and
+    attn_merge_states merges the N states into O and LSE, as a forward whose
+    keys arrive in pieces (sequence sharding) would.  Timed beside the
+    one-shot attn_fwd on the same inputs; kernel times from the library's
+    HIP events (states: the forward kernel kind, merge: the auxiliary kind)."""
+    import torch
+
+    from exact_tiled_softmax_amd import attn
+    from exact_tiled_softmax_amd.inputs import make_tensor
+
+    n = args.state_merge
+    dev = torch.device("cuda:0")
+    print(f"[bench] building inputs for {w.name}", file=sys.stderr, flush=True)
+    q, k, v = (make_tensor(w, nm).to(dev) for nm in ("q", "k", "v"))
+    bounds = [(i * w.Tk // n, (i + 1) * w.Tk // n) for i in range(n)]
+    if any(b <= a for a, b in bounds):
+        print(f"--state-merge {n}: more ranges than keys", file=sys.stderr)
+        return 2
+    # each range's keys as their own buffers, as a shard would hold them
+    ks = [k[:, :, a:b].contiguous() for a, b in bounds]
+    vs = [v[:, :, a:b].contiguous() for a, b in bounds]
+    acc = torch.empty((n, w.B, w.H, w.Tq, w.dv), dtype=torch.float32, device=dev)
+    m = torch.empty((n, w.B, w.H, w.Tq), dtype=torch.float32, device=dev)
+    l = torch.empty_like(m)
+    o = torch.empty((w.B, w.H, w.Tq, w.dv), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.H, w.Tq), dtype=torch.float32, device=dev)
+    o1, lse1 = torch.empty_like(o), torch.empty_like(lse)
+
+    def states():
+        for j, (a, _) in enumerate(bounds):
+            attn.fwd_state(q, ks[j], vs[j], scale=w.scale, causal=w.causal, q_offset=0, k_offset=a, acc=acc[j],
+                           m=m[j], l=l[j])
+        attn.merge_states(acc, m, l, out=o, lse=lse)
+
+    def one_shot():
+        attn.fwd(q, k, v, scale=w.scale, causal=w.causal, out=o1, lse=lse1)
+
+    res = {}
+    for name, fn in (("one_shot", one_shot), ("states", states)):
+        warm_up(fn, args.warmup, args.warmup_min_s)
+        attn.profile_start()
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        attn.profile_stop()
+        res[name] = {kn: attn.profile_query(kind)[0] / args.steps for kind, kn in attn.KERNEL_NAMES.items()
+                     if kn in ("fwd", "fwd_aux")}
+    _, fwd_fl, _, _, _ = work(w)
+    one_ms = res["one_shot"]["fwd"] + res["one_shot"]["fwd_aux"]
+    st_ms, mg_ms = res["states"]["fwd"], res["states"]["fwd_aux"]
+    merge_bytes = n * w.B * w.H * w.Tq * (w.dv + 2) * 4 + w.B * w.H * w.Tq * (w.dv * 2 + 4)
+    do = (o.float() - o1.float()).abs().max().item()
+    dl = (lse - lse1).abs().max().item()
+    line = {
+        "metric": f"attention forward TFLOP/s through {n} key-range states and their merge",
+        "value": round(fwd_fl / ((st_ms + mg_ms) * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "warmup_min_s": args.warmup_min_s,
+        "ms_per_step": round(st_ms + mg_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Tq": w.Tq, "Tk": w.Tk, "d": w.d, "dv": w.dv,
+                   "causal": w.causal, "key_ranges": n, "step": "attn_fwd_state x N + attn_merge_states"},
+        "states": {
+            "states_ms": round(st_ms, 4),
+            "merge_ms": round(mg_ms, 4),
+            "merge_GBs": round(merge_bytes / (mg_ms * 1e-3) / 1e9, 1) if mg_ms > 0 else None,
+            "merge_bytes": merge_bytes,
+            "one_shot_fwd_ms": round(one_ms, 4),
+            "one_shot_tflops": round(fwd_fl / (one_ms * 1e-3) / 1e12, 2),
+            "states_plus_merge_over_one_shot": round((st_ms + mg_ms) / one_ms, 3),
+            "max_abs_diff_o_vs_one_shot": do,
+            "max_abs_diff_lse_vs_one_shot": dl,
+        },
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def warm_up(step, steps, min_s):
     """Run `step` at least `steps` times and, beyond that, until at least
     `min_s` seconds of back-to-back work have run.  From idle the GPU's clock
@@ -466,6 +556,9 @@ def main(argv=None) -> int:
     ap.add_argument("--standard", action="store_true",
                     help="time the tiled forward and the materialised standard forward (attn_fwd_standard) on the "
                          "workload and print the IO comparison line instead of the fwd+bwd step")
+    ap.add_argument("--state-merge", type=int, default=0, metavar="N",
+                    help="time the forward through N key-range states (attn_fwd_state) and their merge "
+                         "(attn_merge_states) beside the one-shot attn_fwd, and print that line instead")
     ap.add_argument("--decode-splits", type=int, default=0,
                     help="decode workloads: key-range splits per sequence (0 = the library's choice)")
     ap.add_argument("--no-targets", dest="targets", action="store_false",
@@ -488,7 +581,8 @@ def main(argv=None) -> int:
     # The CPU oracle runs first: its worker pool forks, which must happen
     # before this process initialises the GPU.
     cpu = None
-    if args.cpu_budget > 0 and not args.copy_calibration and not args.standard and w.dtype == "bf16":
+    if (args.cpu_budget > 0 and not args.copy_calibration and not args.standard and not args.state_merge
+            and w.dtype == "bf16"):
         print(f"[bench] timing the CPU oracle (~{args.cpu_budget:.0f} s)", file=sys.stderr, flush=True)
         cpu = cpu_baseline_decode(w, kv_lens(w), args.cpu_budget) if w.decode else cpu_baseline(w, args.cpu_budget)
 
@@ -510,6 +604,8 @@ def main(argv=None) -> int:
         return bench_decode(args, w, cpu)
     if args.standard:
         return bench_standard(args, w)
+    if args.state_merge > 0:
+        return bench_states(args, w)
     dev = torch.device("cuda:0")
     kern, ms_step, n_warm = time_steps(attn, w, dev, args.steps, args.warmup, args.flush_mib, args.warmup_min_s)
     pairs, fwd_fl, bwd_fl, fwd_b, bwd_b = work(w)

@@ -201,37 +201,51 @@ def bwd(q, k, v, o, lse, dout, scale=None, causal=False, dq=None, dk=None, dv=No
     return dq, dk, dv
 
 
-def fwd_state(q, k, v, scale=None, causal=False, q_offset=0, k_offset=0):
+def fwd_state(q, k, v, scale=None, causal=False, q_offset=0, k_offset=0, acc=None, m=None, l=None):
     """Partial online-softmax state of the keys k, v for the queries q:
-    returns (acc [B,H,Tq,dv] fp32, m [B,H,Tq] fp32 natural-log, l [B,H,Tq] fp32)."""
+    returns (acc [B,H,Tq,dv] fp32, m [B,H,Tq] fp32 natural-log, l [B,H,Tq] fp32),
+    written into acc, m, l when given (e.g. slices of stacked buffers for
+    merge_states)."""
     lib = load()
     B, H, Tq, Tk, d, dv = _dims(q, k, v)
+    _shapes(acc=(acc, (B, H, Tq, dv)), m=(m, (B, H, Tq)), l=(l, (B, H, Tq)))
     dev = q.device
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n, torch.bfloat16, dev)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    acc = torch.empty((B, H, Tq, dv), dtype=torch.float32, device=dev)
-    m = torch.empty((B, H, Tq), dtype=torch.float32, device=dev)
-    l = torch.empty((B, H, Tq), dtype=torch.float32, device=dev)
+    if acc is None:
+        acc = torch.empty((B, H, Tq, dv), dtype=torch.float32, device=dev)
+    if m is None:
+        m = torch.empty((B, H, Tq), dtype=torch.float32, device=dev)
+    if l is None:
+        l = torch.empty((B, H, Tq), dtype=torch.float32, device=dev)
+    _need(acc, "acc", torch.float32, dev, (B, H, Tq, dv))
+    _need(m, "m", torch.float32, dev, (B, H, Tq))
+    _need(l, "l", torch.float32, dev, (B, H, Tq))
     rc = lib.attn_fwd_state(_ptr(q), _ptr(k), _ptr(v), _ptr(acc), _ptr(m), _ptr(l), B, H, Tq, Tk, d, dv,
                             float(scale), int(bool(causal)), int(q_offset), int(k_offset), _stream(dev))
     _check("attn_fwd_state", rc)
     return acc, m, l
 
 
-def merge_states(acc, m, l):
+def merge_states(acc, m, l, out=None, lse=None):
     """Merge n partial states stacked on dim 0 (acc [n,B,H,Tq,dv], m and l
-    [n,B,H,Tq], fp32) into (o [B,H,Tq,dv] bf16, lse [B,H,Tq] fp32)."""
+    [n,B,H,Tq], fp32) into (o [B,H,Tq,dv] bf16, lse [B,H,Tq] fp32), written
+    into out and lse when given."""
     lib = load()
     if acc.dim() != 5 or m.dim() != 4 or l.dim() != 4 or m.shape != acc.shape[:4] or l.shape != m.shape:
         raise ValueError("acc must be [n,B,H,Tq,dv] and m, l [n,B,H,Tq]")
     n, B, H, Tq, dv = acc.shape
+    _shapes(out=(out, (B, H, Tq, dv)), lse=(lse, (B, H, Tq)))
     dev = acc.device
     for t, nm in ((acc, "acc"), (m, "m"), (l, "l")):
         _need(t, nm, torch.float32, dev)
-    o = torch.empty((B, H, Tq, dv), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((B, H, Tq), dtype=torch.float32, device=dev)
+    o = torch.empty((B, H, Tq, dv), dtype=torch.bfloat16, device=dev) if out is None else out
+    if lse is None:
+        lse = torch.empty((B, H, Tq), dtype=torch.float32, device=dev)
+    _need(o, "out", torch.bfloat16, dev, (B, H, Tq, dv))
+    _need(lse, "lse", torch.float32, dev, (B, H, Tq))
     rc = lib.attn_merge_states(_ptr(acc), _ptr(m), _ptr(l), n, _ptr(o), _ptr(lse), B, H, Tq, dv, _stream(dev))
     _check("attn_merge_states", rc)
     return o, lse

@@ -225,6 +225,22 @@ def test_bwd_refuses_misshaped_buffers(lib, which):
         attn.bwd(q, k, v, args["o"], args["lse"], args["dout"], **kw)
 
 
+@pytest.mark.parametrize("which", ["acc", "m", "l"])
+def test_fwd_state_refuses_misshaped_outputs(lib, which):
+    q, k, v = _bf(B_, H_, TQ_, D_), _bf(B_, H_, TK_, D_), _bf(B_, H_, TK_, D_)
+    bad = {"acc": _f32(B_, H_, TQ_, D_ - 1), "m": _f32(B_, H_, TK_), "l": _f32(B_, H_ + 1, TQ_)}[which]
+    with pytest.raises(ValueError, match=f"{which} must have shape"):
+        attn.fwd_state(q, k, v, **{which: bad})
+
+
+@pytest.mark.parametrize("which", ["out", "lse"])
+def test_merge_states_refuses_misshaped_outputs(lib, which):
+    acc, m, l = _f32(3, B_, H_, TQ_, D_), _f32(3, B_, H_, TQ_), _f32(3, B_, H_, TQ_)
+    bad = {"out": _bf(B_, H_, TQ_ + 1, D_), "lse": _f32(B_, H_, TQ_, 1)}[which]
+    with pytest.raises(ValueError, match=f"{which} must have shape"):
+        attn.merge_states(acc, m, l, **{which: bad})
+
+
 def test_f32_and_decode_refuse_misshaped_buffers(lib):
     import torch
     q, k, v = _f32(1, 2, 9, 16), _f32(1, 2, 11, 16), _f32(1, 2, 11, 16)

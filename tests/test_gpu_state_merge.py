@@ -148,3 +148,34 @@ def test_bf16_bwd_zero_lse_gradient_equals_plain_bwd(dev):
     torch.cuda.synchronize()
     for a, b in zip(g0, g1):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_bf16_states_written_into_stacked_buffers(dev):
+    """fwd_state writing into slices of one stacked buffer, and merge_states
+    writing into caller buffers, give bit-for-bit what the allocating calls
+    give (the form the benchmark's key-range path uses)."""
+    cuts = (0, 200, 333, 515)
+    q, k, v, _ = random_problem(14, 1, 3, 300, 515, 128, 128, "bf16")
+    qd = q.to(dev)
+    ks = [k[:, :, a:b].contiguous().to(dev) for a, b in zip(cuts[:-1], cuts[1:])]
+    vs = [v[:, :, a:b].contiguous().to(dev) for a, b in zip(cuts[:-1], cuts[1:])]
+    n = len(ks)
+    acc = torch.full((n, 1, 3, 300, 128), float("nan"), dtype=torch.float32, device=dev)
+    m = torch.full((n, 1, 3, 300), float("nan"), dtype=torch.float32, device=dev)
+    l = torch.full_like(m, float("nan"))
+    sep = []
+    for j, a in enumerate(cuts[:-1]):
+        attn.fwd_state(qd, ks[j], vs[j], causal=True, k_offset=a, acc=acc[j], m=m[j], l=l[j])
+        sep.append(attn.fwd_state(qd, ks[j], vs[j], causal=True, k_offset=a))
+    o = torch.empty((1, 3, 300, 128), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((1, 3, 300), dtype=torch.float32, device=dev)
+    attn.merge_states(acc, m, l, out=o, lse=lse)
+    o2, lse2 = attn.merge_states(torch.stack([s[0] for s in sep]), torch.stack([s[1] for s in sep]),
+                                 torch.stack([s[2] for s in sep]))
+    torch.cuda.synchronize()
+    for j in range(n):
+        assert torch.equal(acc[j], sep[j][0]) and torch.equal(m[j], sep[j][1]) and torch.equal(l[j], sep[j][2])
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, lse2)
+    ro, rl = dense_forward(f64(q), f64(k), f64(v), 1 / math.sqrt(128), True)
+    assert_close("O", f64(o), ro, TOL_BF16)
+    assert_close("LSE", f64(lse), rl, TOL_LSE_BF16)
