@@ -423,13 +423,17 @@ def bench_states(args, w) -> int:
         for j, (a, _) in enumerate(bounds):
             attn.fwd_state(q, ks[j], vs[j], scale=w.scale, causal=w.causal, q_offset=0, k_offset=a, acc=acc[j],
                            m=m[j], l=l[j])
+
+    def merge():
         attn.merge_states(acc, m, l, out=o, lse=lse)
 
     def one_shot():
         attn.fwd(q, k, v, scale=w.scale, causal=w.causal, out=o1, lse=lse1)
 
+    # kernel time per call of each part (a state call that splits its range
+    # launches the forward kernel and a merge of its splits)
     res = {}
-    for name, fn in (("one_shot", one_shot), ("states", states)):
+    for name, fn in (("one_shot", one_shot), ("states", states), ("merge", merge)):
         warm_up(fn, args.warmup, args.warmup_min_s)
         attn.profile_start()
         torch.cuda.synchronize()
@@ -437,11 +441,10 @@ def bench_states(args, w) -> int:
             fn()
         torch.cuda.synchronize()
         attn.profile_stop()
-        res[name] = {kn: attn.profile_query(kind)[0] / args.steps for kind, kn in attn.KERNEL_NAMES.items()
-                     if kn in ("fwd", "fwd_aux")}
+        res[name] = sum(attn.profile_query(kind)[0] for kind, kn in attn.KERNEL_NAMES.items()
+                        if kn in ("fwd", "fwd_aux")) / args.steps
     _, fwd_fl, _, _, _ = work(w)
-    one_ms = res["one_shot"]["fwd"] + res["one_shot"]["fwd_aux"]
-    st_ms, mg_ms = res["states"]["fwd"], res["states"]["fwd_aux"]
+    one_ms, st_ms, mg_ms = res["one_shot"], res["states"], res["merge"]
     merge_bytes = n * w.B * w.H * w.Tq * (w.dv + 2) * 4 + w.B * w.H * w.Tq * (w.dv * 2 + 4)
     do = (o.float() - o1.float()).abs().max().item()
     dl = (lse - lse1).abs().max().item()

@@ -320,8 +320,19 @@ int attn_fwd_state(const void* q, const void* k, const void* v, float* acc, floa
   const long long diag = (long long)q_offset - (long long)k_offset;
   const long long lim = 1LL << 30;
   const int diag_c = (int)(diag > lim ? lim : (diag < -lim ? -lim : diag));
-  hipError_t e = attn::fwd_bf16_state_launch(q, k, v, acc, m, l, B * H, Tq, Tk, d, scale, causal, diag_c,
-                                             static_cast<hipStream_t>(stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int BH = B * H;
+  const int splits = attn::fwd_bf16_state_splits(BH, Tq, Tk, causal);
+  void* ws = nullptr;
+  if (splits > 1) {
+    hipError_t e = ws_alloc(&ws, attn::fwd_bf16_workspace_bytes(BH, Tq, Tk, d, splits), s);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  hipError_t e = attn::fwd_bf16_state_launch(q, k, v, acc, m, l, BH, Tq, Tk, d, scale, causal, diag_c, splits, ws, s);
+  if (ws) {
+    hipError_t f = hipFreeAsync(ws, s);
+    if (e == hipSuccess) e = f;
+  }
   return e == hipSuccess ? ATTN_OK : hip_fail(e);
 }
 

@@ -59,10 +59,13 @@ hipError_t fwd_bf16_launch(const void* q, const void* k, const void* v, void* o,
                            int Tk, int d, float scale, int causal, int num_splits, void* workspace,
                            hipStream_t stream);
 // Partial state (acc, m, l) of one key range; causal blocks key j for query i
-// when j > i + diag.  m in natural-log units.
-// (no workspace)
+// when j > i + diag.  m in natural-log units.  With num_splits > 1 the range
+// is computed in key splits (workspace of fwd_bf16_workspace_bytes) whose
+// states are merged into acc, m, l; fwd_bf16_state_splits gives the count.
+int fwd_bf16_state_splits(int BH, int Tq, int Tk, int causal);
 hipError_t fwd_bf16_state_launch(const void* q, const void* k, const void* v, float* acc, float* m, float* l, int BH,
-                                 int Tq, int Tk, int d, float scale, int causal, int diag, hipStream_t stream);
+                                 int Tq, int Tk, int d, float scale, int causal, int diag, int num_splits,
+                                 void* workspace, hipStream_t stream);
 // Merge of n partial states [n][BH][Tq](x d) into O (bf16) and LSE.
 hipError_t merge_states_launch(const float* acc, const float* m, const float* l, int n, void* o, float* lse, int BH,
                                int Tq, int d, hipStream_t stream);

@@ -489,12 +489,16 @@ __global__ __launch_bounds__(FwdCfg<D>::THREADS, FwdCfg<D>::WAVES_PER_SIMD) void
 //   O = a / l, LSE = M + ln l.  D/4 lanes per row, each with 4 consecutive
 // columns, so that every partial accumulator is read with 16-byte loads (with
 // one wave per row and 4-byte loads the merge ran at 3.3-3.6 TB/s).
-template <int D>
+// With STATE the merged state itself is written (acc = a, m = M, l) instead
+// of O and LSE: a key-range state computed in splits.
+template <int D, bool STATE>
 __global__ __launch_bounds__(256) void fwd_combine_kernel(const float* __restrict__ part_acc,
                                                           const float* __restrict__ part_m,
                                                           const float* __restrict__ part_l,
                                                           __bf16* __restrict__ o, float* __restrict__ lse,
-                                                          int BH, int Tq, int num_splits) {
+                                                          float* __restrict__ st_acc, float* __restrict__ st_m,
+                                                          float* __restrict__ st_l, int BH, int Tq,
+                                                          int num_splits) {
   constexpr int LPR = D / 4;  // lanes per row
   const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t rowid = t / LPR;
@@ -512,10 +516,18 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(const float* __restric
     const f32x4 pa = *reinterpret_cast<const f32x4*>(part_acc + (s * stride + rowid) * D + c);
     acc += w * pa;
   }
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  const u32x2 ov = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
-  *reinterpret_cast<u32x2*>(o + rowid * D + c) = ov;
-  if (c == 0) lse[rowid] = l > 0.f ? M + fast_log2(l) * kLn2 : -INFINITY;
+  if constexpr (STATE) {
+    *reinterpret_cast<f32x4*>(st_acc + rowid * D + c) = acc;
+    if (c == 0) {
+      st_m[rowid] = M;
+      st_l[rowid] = l;
+    }
+  } else {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const u32x2 ov = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+    *reinterpret_cast<u32x2*>(o + rowid * D + c) = ov;
+    if (c == 0) lse[rowid] = l > 0.f ? M + fast_log2(l) * kLn2 : -INFINITY;
+  }
 }
 
 template <int D, bool CAUSAL, bool SPLIT>
@@ -622,11 +634,11 @@ hipError_t merge_states_launch(const float* acc, const float* m, const float* l,
   const unsigned blocks = (unsigned)(((size_t)BH * Tq * (d / 4) + 255) / 256);
   prof_begin(1, stream);
   if (d == 128)
-    hipLaunchKernelGGL(fwd_combine_kernel<128>, dim3(blocks), dim3(256), 0, stream, acc, m, l,
-                       static_cast<__bf16*>(o), lse, BH, Tq, n);
+    hipLaunchKernelGGL((fwd_combine_kernel<128, false>), dim3(blocks), dim3(256), 0, stream, acc, m, l,
+                       static_cast<__bf16*>(o), lse, nullptr, nullptr, nullptr, BH, Tq, n);
   else
-    hipLaunchKernelGGL(fwd_combine_kernel<64>, dim3(blocks), dim3(256), 0, stream, acc, m, l,
-                       static_cast<__bf16*>(o), lse, BH, Tq, n);
+    hipLaunchKernelGGL((fwd_combine_kernel<64, false>), dim3(blocks), dim3(256), 0, stream, acc, m, l,
+                       static_cast<__bf16*>(o), lse, nullptr, nullptr, nullptr, BH, Tq, n);
   prof_end(1, stream);
   return hipGetLastError();
 }
@@ -648,13 +660,39 @@ hipError_t fwd_bf16_launch(const void* q, const void* k, const void* v, void* o,
   return merge_states_launch(args.part_acc, args.part_m, args.part_l, num_splits, o, lse, BH, Tq, d, stream);
 }
 
+int fwd_bf16_state_splits(int BH, int Tq, int Tk, int causal) {
+  // the forward's own rule (key splits only without the mask)
+  return fwd_bf16_num_splits(BH, Tq, Tk, causal, 0);
+}
+
 hipError_t fwd_bf16_state_launch(const void* q, const void* k, const void* v, float* acc, float* m, float* l, int BH,
-                                 int Tq, int Tk, int d, float scale, int causal, int diag, hipStream_t stream) {
-  FwdArgs args = fwd_args(q, k, v, nullptr, nullptr, BH, Tq, Tk, scale, 1, diag);
-  args.part_acc = acc;
-  args.part_m = m;
-  args.part_l = l;
-  return fwd_run(args, d, causal != 0, true, stream);
+                                 int Tq, int Tk, int d, float scale, int causal, int diag, int num_splits,
+                                 void* workspace, hipStream_t stream) {
+  FwdArgs args = fwd_args(q, k, v, nullptr, nullptr, BH, Tq, Tk, scale, num_splits, diag);
+  if (num_splits <= 1) {
+    args.part_acc = acc;
+    args.part_m = m;
+    args.part_l = l;
+    return fwd_run(args, d, causal != 0, true, stream);
+  }
+  // the key range in splits, then the split states merged into one state
+  const FwdLayout L = fwd_layout(BH, Tq, Tk, d, num_splits);
+  char* ws = static_cast<char*>(workspace);
+  args.part_acc = reinterpret_cast<float*>(ws + L.part_acc);
+  args.part_m = reinterpret_cast<float*>(ws + L.part_m);
+  args.part_l = reinterpret_cast<float*>(ws + L.part_l);
+  hipError_t e = fwd_run(args, d, causal != 0, true, stream);
+  if (e != hipSuccess) return e;
+  const unsigned blocks = (unsigned)(((size_t)BH * Tq * (d / 4) + 255) / 256);
+  prof_begin(1, stream);
+  if (d == 128)
+    hipLaunchKernelGGL((fwd_combine_kernel<128, true>), dim3(blocks), dim3(256), 0, stream, args.part_acc,
+                       args.part_m, args.part_l, nullptr, nullptr, acc, m, l, BH, Tq, num_splits);
+  else
+    hipLaunchKernelGGL((fwd_combine_kernel<64, true>), dim3(blocks), dim3(256), 0, stream, args.part_acc,
+                       args.part_m, args.part_l, nullptr, nullptr, acc, m, l, BH, Tq, num_splits);
+  prof_end(1, stream);
+  return hipGetLastError();
 }
 
 }  // namespace attn

@@ -205,7 +205,12 @@ int attn_bwd_dlse(const void* q, const void* k, const void* v, const void* o, co
  *               first key; with causal != 0, key j is blocked for query i when
  *               k_offset + j > q_offset + i (the top-left rule of attn_fwd on
  *               global indices).  Ignored when causal == 0.
- * Supported: d == dv, d in {64, 128}.  No workspace.
+ * Supported: d == dv, d in {64, 128}.  Workspace: none, except without the
+ * causal mask when the query tiles alone would leave the chip under-filled
+ * (few queries, many keys): then the key range is computed in splits, as in
+ * attn_fwd, whose partial states (splits*B*H*Tq*(dv+2) floats, from the
+ * library's workspace pool on `stream`) are merged into acc, m, l by the rule
+ * of attn_merge_states.
  */
 int attn_fwd_state(const void* q, const void* k, const void* v, float* acc, float* m, float* l,
                    int B, int H, int Tq, int Tk, int d, int dv, float scale, int causal,

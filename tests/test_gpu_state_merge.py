@@ -179,3 +179,24 @@ def test_bf16_states_written_into_stacked_buffers(dev):
     ro, rl = dense_forward(f64(q), f64(k), f64(v), 1 / math.sqrt(128), True)
     assert_close("O", f64(o), ro, TOL_BF16)
     assert_close("LSE", f64(lse), rl, TOL_LSE_BF16)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bf16_state_of_a_long_range_computed_in_splits(dev, d):
+    """Few queries against a long key range without the mask: the call splits
+    the range inside (as the forward does) and merges the split states into
+    one state, which must still be the exact state of the whole range."""
+    B, H, Tq, Tk = 1, 2, 100, 4200
+    q, k, v, _ = random_problem(15, B, H, Tq, Tk, d, d, "bf16", sigma_q=1.5)
+    scale = 1 / math.sqrt(d)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    acc, m, l = attn.fwd_state(qd, kd, vd, causal=False)
+    o, lse = attn.merge_states(acc[None], m[None], l[None])
+    torch.cuda.synchronize()
+    ref = attention_state(f64(q), f64(k), f64(v), scale, False)
+    bh = lambda x: x.reshape((B * H,) + x.shape[2:])
+    for h in range(B * H):
+        check_state(f"head {h}", tuple(bh(x)[h] for x in (acc, m, l)), tuple(bh(x)[h] for x in ref))
+    ro, rl = dense_forward(f64(q), f64(k), f64(v), scale, False)
+    assert_close("O", f64(o), ro, TOL_BF16)
+    assert_close("LSE", f64(lse), rl, TOL_LSE_BF16)
